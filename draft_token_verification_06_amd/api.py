@@ -1,0 +1,212 @@
+"""Python binding of the C ABI in include/sv.h: argument marshalling only.
+
+Tensors must live on a ROCm device; every computation runs in the HIP
+library on the current torch stream of that device.  Results come back as
+device tensors; nothing synchronises.
+"""
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from ._lib import lib
+
+SV_OP_WINDOW, SV_OP_GREEDY, SV_OP_TREE = 0, 1, 2
+SV_TREE_GREEDY, SV_TREE_STOCHASTIC = 0, 1
+_DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+
+
+class SvError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__(f"specverify status {status}: {lib().sv_strerror(status).decode()}")
+
+
+def _check(status):
+    if status != 0:
+        raise SvError(status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _logits(t, rows, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in _DTYPE_CODE:
+        raise ValueError(f"{name}: dtype {t.dtype} is not float32, bfloat16 or float16")
+    if t.dim() != 3 or t.shape[1] != rows:
+        raise ValueError(f"{name}: expected shape (B, {rows}, V), got {tuple(t.shape)}")
+    V = t.shape[2]
+    if t.stride(2) != 1 or t.stride(1) != V:
+        raise ValueError(f"{name}: rows of one sequence must be contiguous")
+    return t.stride(0)
+
+
+def _i32(t, shape, name):
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected a contiguous int32 device tensor of shape {tuple(shape)}")
+
+
+def _optional(t, dtype, B, name):
+    if t is None:
+        return None
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != (B,):
+        raise ValueError(f"{name}: expected a contiguous {dtype} device tensor of shape ({B},)")
+    return t
+
+
+def workspace_size(op, B, n, V, dtype):
+    return int(lib().sv_workspace_size(op, B, n, V, _DTYPE_CODE[dtype]))
+
+
+def workspace(op, B, n, V, dtype, device):
+    nbytes = workspace_size(op, B, n, V, dtype)
+    if nbytes == 0:
+        raise ValueError("invalid sizes for a workspace")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+@dataclass
+class WindowResult:
+    n_accepted: torch.Tensor
+    out_tokens: torch.Tensor
+    p_draft: Optional[torch.Tensor] = None
+    q_draft: Optional[torch.Tensor] = None
+
+
+@dataclass
+class TreeResult:
+    n_accepted: torch.Tensor
+    best_node: torch.Tensor
+    out_tokens: torch.Tensor
+    out_nodes: torch.Tensor
+
+
+def verify_window(target, draft, tokens, *, seed=0, tag=0, window_len=None, seq_ids=None,
+                  base_pos=None, return_probs=False, ws=None, out=None):
+    """Stochastic window verification: sv_verify_window."""
+    B, rows, V = target.shape
+    gamma = rows - 1
+    ts = _logits(target, gamma + 1, "target")
+    ds = _logits(draft, gamma, "draft")
+    if draft.dtype != target.dtype or draft.shape[0] != B or draft.shape[2] != V:
+        raise ValueError("draft must match target in dtype, batch and vocabulary")
+    _i32(tokens, (B, gamma), "tokens")
+    _optional(window_len, torch.int32, B, "window_len")
+    _optional(seq_ids, torch.int64, B, "seq_ids")
+    _optional(base_pos, torch.int64, B, "base_pos")
+    dev = target.device
+    if ws is None:
+        ws = workspace(SV_OP_WINDOW, B, gamma, V, target.dtype, dev)
+    if out is None:
+        out = WindowResult(torch.empty(B, dtype=torch.int32, device=dev),
+                           torch.empty(B, gamma + 1, dtype=torch.int32, device=dev))
+        if return_probs:
+            out.p_draft = torch.empty(B, gamma, dtype=torch.float32, device=dev)
+            out.q_draft = torch.empty(B, gamma, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().sv_verify_window(
+            _ptr(target), ts, _ptr(draft), ds, _DTYPE_CODE[target.dtype],
+            _ptr(tokens), _ptr(window_len), B, gamma, V,
+            ctypes.c_uint64(seed), ctypes.c_uint64(tag), _ptr(seq_ids), _ptr(base_pos),
+            _ptr(out.n_accepted), _ptr(out.out_tokens), _ptr(out.p_draft), _ptr(out.q_draft),
+            _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def verify_greedy(target, tokens, *, window_len=None, ws=None, out=None):
+    """Greedy window verification: sv_verify_greedy."""
+    B, rows, V = target.shape
+    gamma = rows - 1
+    ts = _logits(target, gamma + 1, "target")
+    _i32(tokens, (B, gamma), "tokens")
+    _optional(window_len, torch.int32, B, "window_len")
+    dev = target.device
+    if ws is None:
+        ws = workspace(SV_OP_GREEDY, B, gamma, V, target.dtype, dev)
+    if out is None:
+        out = WindowResult(torch.empty(B, dtype=torch.int32, device=dev),
+                           torch.empty(B, gamma + 1, dtype=torch.int32, device=dev))
+    with torch.cuda.device(dev):
+        _check(lib().sv_verify_greedy(
+            _ptr(target), ts, _DTYPE_CODE[target.dtype], _ptr(tokens), _ptr(window_len),
+            B, gamma, V, _ptr(out.n_accepted), _ptr(out.out_tokens),
+            _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def tree_max_depth(parent):
+    arr = (ctypes.c_int32 * len(parent))(*parent)
+    d = lib().sv_tree_max_depth(arr, len(parent))
+    if d < 0:
+        raise SvError(d)
+    return d
+
+
+def verify_tree(target, draft, node_tokens, parent, *, mode="stochastic", seed=0, tag=0,
+                seq_ids=None, base_pos=None, ws=None):
+    """Token-tree verification: sv_verify_tree.  parent is a host sequence."""
+    B, N, V = target.shape
+    if len(parent) != N:
+        raise ValueError("parent must have one entry per tree node")
+    if target.stride(2) != 1 or target.stride(1) != V or target.stride(0) != N * V:
+        raise ValueError("target must be contiguous (B, N, V)")
+    code = SV_TREE_STOCHASTIC if mode == "stochastic" else SV_TREE_GREEDY
+    if code == SV_TREE_STOCHASTIC:
+        if draft is None or draft.shape != target.shape or draft.dtype != target.dtype \
+                or not draft.is_contiguous():
+            raise ValueError("stochastic mode needs contiguous draft logits shaped like target")
+    _i32(node_tokens, (B, N), "node_tokens")
+    _optional(seq_ids, torch.int64, B, "seq_ids")
+    _optional(base_pos, torch.int64, B, "base_pos")
+    D = tree_max_depth(parent)
+    dev = target.device
+    if ws is None:
+        ws = workspace(SV_OP_TREE, B, N, V, target.dtype, dev)
+    res = TreeResult(torch.empty(B, dtype=torch.int32, device=dev),
+                     torch.empty(B, dtype=torch.int32, device=dev),
+                     torch.empty(B, D + 1, dtype=torch.int32, device=dev),
+                     torch.empty(B, max(D, 1), dtype=torch.int32, device=dev)[:, :D])
+    par = (ctypes.c_int32 * N)(*parent)
+    with torch.cuda.device(dev):
+        _check(lib().sv_verify_tree(
+            _ptr(target), _ptr(draft if code == SV_TREE_STOCHASTIC else None),
+            _DTYPE_CODE[target.dtype], _ptr(node_tokens), par, B, N, V, code,
+            ctypes.c_uint64(seed), ctypes.c_uint64(tag), _ptr(seq_ids), _ptr(base_pos),
+            _ptr(res.n_accepted), _ptr(res.best_node), _ptr(res.out_tokens), _ptr(res.out_nodes),
+            _ptr(ws), ws.numel(), _stream(dev)))
+    return res
+
+
+def rollback(buf_tokens, buf_len, stage, verified, verified_len, *, len_offset=0):
+    """Per-stage buffer rollback: sv_rollback (in place on buf_tokens/buf_len)."""
+    S, K, cap = buf_tokens.shape
+    _i32(buf_tokens, (S, K, cap), "buf_tokens")
+    _i32(buf_len, (S, K), "buf_len")
+    if verified.dtype != torch.int32 or not verified.is_cuda or verified.dim() != 2 \
+            or verified.shape[0] != S or verified.stride(1) != 1:
+        raise ValueError("verified: expected an int32 device tensor (S, >=L) with unit column stride")
+    _i32(verified_len, (S,), "verified_len")
+    dev = buf_tokens.device
+    with torch.cuda.device(dev):
+        _check(lib().sv_rollback(
+            _ptr(buf_tokens), _ptr(buf_len), S, K, cap, stage,
+            _ptr(verified), verified.stride(0), _ptr(verified_len), len_offset, _stream(dev)))
+
+
+def probe_read(buf, sink=None):
+    """Streams buf through the library's read-bandwidth probe kernel."""
+    nbytes = buf.numel() * buf.element_size()
+    nb = int(lib().sv_probe_blocks(nbytes))
+    if sink is None:
+        sink = torch.empty(nb, dtype=torch.int32, device=buf.device)
+    with torch.cuda.device(buf.device):
+        _check(lib().sv_probe_read(_ptr(buf), nbytes, _ptr(sink), _stream(buf.device)))
+    return sink

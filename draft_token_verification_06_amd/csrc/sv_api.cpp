@@ -1,0 +1,319 @@
+// C-ABI entry points of libspecverify.so: argument validation, workspace
+// carving and kernel dispatch.  No allocation, no synchronisation; every
+// launch goes to the caller's stream.
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/sv.h"
+#include "sv_launch.h"
+#include "sv_plan.h"
+
+using namespace sv;
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+int elem_bytes(int dtype) {
+  switch (dtype) {
+    case SV_DT_F32: return 4;
+    case SV_DT_BF16:
+    case SV_DT_F16: return 2;
+    default: return 0;
+  }
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_workspace(void *ws, size_t bytes, size_t need) {
+  if (need == 0) return SV_EINVAL;
+  if (!ws || !aligned(ws, 256) || bytes < need) return SV_EWORKSPACE;
+  return SV_OK;
+}
+
+int launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? SV_OK : SV_ELAUNCH;
+}
+
+// Builds the tree description; returns SV_OK or SV_ETREE.
+int build_tree(const int32_t *parent, int32_t N, TreeMeta *meta) {
+  if (!parent || N < 1 || N > kTreeMaxNodes) return SV_ETREE;
+  if (parent[0] != -1) return SV_ETREE;
+  std::memset(meta, 0, sizeof(*meta));
+  meta->N = N;
+  int count_at[kTreeMaxNodes + 1] = {0};
+  count_at[0] = 1;
+  meta->parent[0] = -1;
+  int max_depth = 0;
+  for (int v = 1; v < N; ++v) {
+    const int w = parent[v];
+    if (w < 0 || w >= v) return SV_ETREE;
+    const int d = meta->depth[w] + 1;
+    if (d > kTreeMaxDepth) return SV_ETREE;
+    meta->parent[v] = static_cast<int16_t>(w);
+    meta->depth[v] = static_cast<uint8_t>(d);
+    meta->rank[v] = static_cast<int16_t>(count_at[d]++);
+    meta->internal[w >> 6] |= 1ull << (w & 63);
+    if (d > max_depth) max_depth = d;
+  }
+  meta->max_depth = max_depth;
+  return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sv_version(void) { return kVersion; }
+
+const char *sv_strerror(int status) {
+  switch (status) {
+    case SV_OK: return "ok";
+    case SV_EINVAL: return "invalid argument (size, null or misaligned pointer)";
+    case SV_EDTYPE: return "unknown logits dtype";
+    case SV_EWORKSPACE: return "workspace missing, not 256-byte aligned, or too small";
+    case SV_ETREE: return "malformed tree (parent[0] != -1, parent[v] not in [0, v), too many nodes or too deep)";
+    case SV_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t sv_workspace_size(int op, int32_t B, int32_t n, int32_t V, int dtype) {
+  if (elem_bytes(dtype) == 0 || B < 1 || V < 1) return 0;
+  if (op == SV_OP_WINDOW || op == SV_OP_GREEDY) {
+    if (n < 1 || n > SV_MAX_GAMMA) return 0;
+  } else if (op == SV_OP_TREE) {
+    if (n < 1 || n > SV_TREE_MAX_NODES) return 0;
+  } else {
+    return 0;
+  }
+  return make_layout(op, B, n, V).total;
+}
+
+int sv_verify_window(const void *target_logits, int64_t target_seq_stride,
+                     const void *draft_logits, int64_t draft_seq_stride, int dtype,
+                     const int32_t *draft_tokens, const int32_t *window_len,
+                     int32_t B, int32_t gamma, int32_t V,
+                     uint64_t seed, uint64_t tag, const uint64_t *seq_ids,
+                     const int64_t *base_pos,
+                     int32_t *n_accepted, int32_t *out_tokens,
+                     float *p_draft, float *q_draft,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return SV_EDTYPE;
+  if (B < 1 || gamma < 1 || gamma > SV_MAX_GAMMA || V < 1) return SV_EINVAL;
+  if (!target_logits || !draft_logits || !draft_tokens || !n_accepted || !out_tokens) return SV_EINVAL;
+  if (!aligned(target_logits, eb) || !aligned(draft_logits, eb)) return SV_EINVAL;
+  const int64_t t_rows = static_cast<int64_t>(gamma + 1) * V;
+  const int64_t d_rows = static_cast<int64_t>(gamma) * V;
+  if (target_seq_stride == 0) target_seq_stride = t_rows;
+  if (draft_seq_stride == 0) draft_seq_stride = d_rows;
+  if (target_seq_stride < t_rows || draft_seq_stride < d_rows) return SV_EINVAL;
+  const Layout L = make_layout(SV_OP_WINDOW, B, gamma, V);
+  const int ws = check_workspace(workspace, workspace_bytes, L.total);
+  if (ws != SV_OK) return ws;
+
+  char *wsb = static_cast<char *>(workspace);
+  float2 *part = reinterpret_cast<float2 *>(wsb + L.part_off);
+  SampleJob *jobs = reinterpret_cast<SampleJob *>(wsb + L.jobs_off);
+  float *spart = reinterpret_cast<float *>(wsb + L.spart_off);
+
+  RowSet rs{};
+  rs.t = static_cast<const char *>(target_logits);
+  rs.t_stride_bytes = target_seq_stride * eb;
+  rs.d = static_cast<const char *>(draft_logits);
+  rs.d_stride_bytes = draft_seq_stride * eb;
+  rs.rows_t = gamma + 1;
+  rs.rows_d = gamma;
+  rs.window_len = window_len;
+  rs.gamma = gamma;
+  rs.V = V;
+  rs.S = L.plan.S;
+  rs.seg_len = L.plan.seg_len;
+  for (auto &m : rs.dmask) m = ~0ull;
+  launch_row_stats(dtype, false, rs, static_cast<int64_t>(B) * L.rows_per_seq * L.plan.S, part, stream);
+
+  WindowArgs A{};
+  A.t = rs.t;
+  A.t_stride_bytes = rs.t_stride_bytes;
+  A.d = rs.d;
+  A.d_stride_bytes = rs.d_stride_bytes;
+  A.tokens = draft_tokens;
+  A.window_len = window_len;
+  A.gamma = gamma;
+  A.V = V;
+  A.S = L.plan.S;
+  A.seed = seed;
+  A.tag = tag;
+  A.seq_ids = seq_ids;
+  A.base_pos = base_pos;
+  A.part = part;
+  A.n_accepted = n_accepted;
+  A.out_tokens = out_tokens;
+  A.p_draft = p_draft;
+  A.q_draft = q_draft;
+  A.jobs = jobs;
+  launch_window_decide(dtype, A, B, stream);
+  launch_sample(dtype, jobs, B, V, L.chunks, spart, stream);
+  return launch_status();
+}
+
+int sv_verify_greedy(const void *target_logits, int64_t target_seq_stride, int dtype,
+                     const int32_t *draft_tokens, const int32_t *window_len,
+                     int32_t B, int32_t gamma, int32_t V,
+                     int32_t *n_accepted, int32_t *out_tokens,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return SV_EDTYPE;
+  if (B < 1 || gamma < 1 || gamma > SV_MAX_GAMMA || V < 1) return SV_EINVAL;
+  if (!target_logits || !draft_tokens || !n_accepted || !out_tokens) return SV_EINVAL;
+  if (!aligned(target_logits, eb)) return SV_EINVAL;
+  const int64_t t_rows = static_cast<int64_t>(gamma + 1) * V;
+  if (target_seq_stride == 0) target_seq_stride = t_rows;
+  if (target_seq_stride < t_rows) return SV_EINVAL;
+  const Layout L = make_layout(SV_OP_GREEDY, B, gamma, V);
+  const int ws = check_workspace(workspace, workspace_bytes, L.total);
+  if (ws != SV_OK) return ws;
+  float2 *part = reinterpret_cast<float2 *>(static_cast<char *>(workspace) + L.part_off);
+
+  RowSet rs{};
+  rs.t = static_cast<const char *>(target_logits);
+  rs.t_stride_bytes = target_seq_stride * eb;
+  rs.d = nullptr;
+  rs.rows_t = gamma + 1;
+  rs.rows_d = 0;
+  rs.window_len = window_len;
+  rs.gamma = gamma;
+  rs.V = V;
+  rs.S = L.plan.S;
+  rs.seg_len = L.plan.seg_len;
+  launch_row_stats(dtype, true, rs, static_cast<int64_t>(B) * L.rows_per_seq * L.plan.S, part, stream);
+
+  GreedyArgs A{};
+  A.tokens = draft_tokens;
+  A.window_len = window_len;
+  A.gamma = gamma;
+  A.V = V;
+  A.S = L.plan.S;
+  A.part = part;
+  A.n_accepted = n_accepted;
+  A.out_tokens = out_tokens;
+  launch_greedy_decide(A, B, stream);
+  return launch_status();
+}
+
+int32_t sv_tree_max_depth(const int32_t *parent_host, int32_t N) {
+  TreeMeta meta;
+  const int st = build_tree(parent_host, N, &meta);
+  return st == SV_OK ? meta.max_depth : st;
+}
+
+int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtype,
+                   const int32_t *node_tokens, const int32_t *parent_host,
+                   int32_t B, int32_t N, int32_t V, int mode,
+                   uint64_t seed, uint64_t tag, const uint64_t *seq_ids,
+                   const int64_t *base_pos,
+                   int32_t *n_accepted, int32_t *best_node,
+                   int32_t *out_tokens, int32_t *out_nodes,
+                   void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return SV_EDTYPE;
+  if (B < 1 || V < 1 || (mode != SV_TREE_GREEDY && mode != SV_TREE_STOCHASTIC)) return SV_EINVAL;
+  TreeMeta meta;
+  const int tst = build_tree(parent_host, N, &meta);
+  if (tst != SV_OK) return tst;
+  if (!target_logits || !node_tokens || !n_accepted || !best_node || !out_tokens) return SV_EINVAL;
+  if (meta.max_depth > 0 && !out_nodes) return SV_EINVAL;
+  if (mode == SV_TREE_STOCHASTIC && !draft_logits) return SV_EINVAL;
+  if (!aligned(target_logits, eb) || (draft_logits && !aligned(draft_logits, eb))) return SV_EINVAL;
+  const Layout L = make_layout(SV_OP_TREE, B, N, V);
+  const int ws = check_workspace(workspace, workspace_bytes, L.total);
+  if (ws != SV_OK) return ws;
+  char *wsb = static_cast<char *>(workspace);
+  float2 *part = reinterpret_cast<float2 *>(wsb + L.part_off);
+  SampleJob *jobs = reinterpret_cast<SampleJob *>(wsb + L.jobs_off);
+  float *spart = reinterpret_cast<float *>(wsb + L.spart_off);
+
+  const int64_t seq_bytes = static_cast<int64_t>(N) * V * eb;
+  RowSet rs{};
+  rs.t = static_cast<const char *>(target_logits);
+  rs.t_stride_bytes = seq_bytes;
+  rs.d = static_cast<const char *>(draft_logits);
+  rs.d_stride_bytes = seq_bytes;
+  rs.rows_t = N;
+  rs.rows_d = (mode == SV_TREE_STOCHASTIC) ? N : 0;
+  rs.window_len = nullptr;
+  rs.gamma = 0;
+  rs.V = V;
+  rs.S = L.plan.S;
+  rs.seg_len = L.plan.seg_len;
+  for (int k = 0; k < kTreeMaxNodes / 64; ++k) rs.dmask[k] = meta.internal[k];
+  // The plan is laid out for 2N rows per sequence; greedy launches only the
+  // first N of them (target rows) but keeps the same partial-row indexing.
+  const int R = 2 * N;
+  if (mode == SV_TREE_STOCHASTIC) {
+    launch_row_stats(dtype, false, rs, static_cast<int64_t>(B) * R * L.plan.S, part, stream);
+  } else {
+    RowSet g = rs;
+    g.rows_d = N;  // keep the 2N-row indexing; draft rows are masked off
+    for (auto &m : g.dmask) m = 0;
+    launch_row_stats(dtype, true, g, static_cast<int64_t>(B) * R * L.plan.S, part, stream);
+  }
+
+  TreeArgs A{};
+  A.t = rs.t;
+  A.d = rs.d;
+  A.seq_bytes = seq_bytes;
+  A.tokens = node_tokens;
+  A.V = V;
+  A.S = L.plan.S;
+  A.R = R;
+  A.mode = mode == SV_TREE_STOCHASTIC ? 1 : 0;
+  A.seed = seed;
+  A.tag = tag;
+  A.seq_ids = seq_ids;
+  A.base_pos = base_pos;
+  A.part = part;
+  A.n_accepted = n_accepted;
+  A.best_node = best_node;
+  A.out_tokens = out_tokens;
+  A.out_nodes = out_nodes;
+  A.jobs = jobs;
+  A.meta = meta;
+  launch_tree_decide(dtype, A, B, stream);
+  if (mode == SV_TREE_STOCHASTIC) launch_sample(dtype, jobs, B, V, L.chunks, spart, stream);
+  return launch_status();
+}
+
+int sv_rollback(int32_t *buf_tokens, int32_t *buf_len, int32_t S, int32_t K,
+                int32_t cap, int32_t stage,
+                const int32_t *verified_tokens, int64_t verified_stride,
+                const int32_t *verified_len, int32_t len_offset,
+                hipStream_t stream) {
+  if (S < 1 || K < 2 || cap < 1 || stage < 1 || stage >= K) return SV_EINVAL;
+  if (stage > 65535) return SV_EINVAL;
+  if (!buf_tokens || !buf_len || !verified_tokens || !verified_len) return SV_EINVAL;
+  if (verified_stride < 0) return SV_EINVAL;
+  RollbackArgs A{};
+  A.buf_tokens = buf_tokens;
+  A.buf_len = buf_len;
+  A.K = K;
+  A.cap = cap;
+  A.verified = verified_tokens;
+  A.verified_stride = verified_stride;
+  A.verified_len = verified_len;
+  A.len_offset = len_offset;
+  launch_rollback(A, S, stage, stream);
+  return launch_status();
+}
+
+int32_t sv_probe_blocks(size_t bytes) { return probe_blocks(bytes); }
+
+int sv_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream) {
+  if (!src || !sink || bytes < 16 || bytes % 16 != 0 || !aligned(src, 16)) return SV_EINVAL;
+  launch_probe_read(src, bytes, sink, stream);
+  return launch_status();
+}
+
+}  // extern "C"

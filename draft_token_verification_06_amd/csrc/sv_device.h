@@ -1,0 +1,162 @@
+// Device helpers of the verification kernels (gfx950, wave64).
+//
+// Logit decoding, the Philox4x64-10 uniform stream, and the fixed-order
+// (max, sum-exp) / (max, first-index) combines used by every reduction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+// ---------------------------------------------------------------------------
+// Logit decoding.  A 16-byte vector holds EPV elements; decoding is exact.
+// ---------------------------------------------------------------------------
+template <int DT> struct Elt;
+
+template <> struct Elt<DT_BF16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kEPV = 8;
+  static constexpr uint32_t kNegInfPair = 0xFF80FF80u;  // two bf16 -inf
+  __device__ static __forceinline__ float one(const void *row, int64_t i) {
+    const uint32_t r = reinterpret_cast<const uint16_t *>(row)[i];
+    return __uint_as_float(r << 16);
+  }
+  __device__ static __forceinline__ void vec(const uint4 &r, float *x) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(w[k] << 16);
+      x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  }
+};
+
+template <> struct Elt<DT_F16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kEPV = 8;
+  static constexpr uint32_t kNegInfPair = 0xFC00FC00u;  // two f16 -inf
+  __device__ static __forceinline__ float h2f(uint32_t bits) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+  }
+  __device__ static __forceinline__ float one(const void *row, int64_t i) {
+    return h2f(reinterpret_cast<const uint16_t *>(row)[i]);
+  }
+  __device__ static __forceinline__ void vec(const uint4 &r, float *x) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = h2f(w[k] & 0xFFFFu);
+      x[2 * k + 1] = h2f(w[k] >> 16);
+    }
+  }
+};
+
+template <> struct Elt<DT_F32> {
+  static constexpr int kBytes = 4;
+  static constexpr int kEPV = 4;
+  static constexpr uint32_t kNegInfPair = 0xFF800000u;  // one f32 -inf
+  __device__ static __forceinline__ float one(const void *row, int64_t i) {
+    return reinterpret_cast<const float *>(row)[i];
+  }
+  __device__ static __forceinline__ void vec(const uint4 &r, float *x) {
+    x[0] = __uint_as_float(r.x);
+    x[1] = __uint_as_float(r.y);
+    x[2] = __uint_as_float(r.z);
+    x[3] = __uint_as_float(r.w);
+  }
+};
+
+// 2^x on the hardware transcendental unit (v_exp_f32).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// exp(x - m) evaluated as 2^(x*log2e - m*log2e); every kernel uses this one
+// form so numerators and normalisers carry the same rounding of m*log2e.
+__device__ __forceinline__ float exp_shift(float x, float m_log2e) {
+  return exp2_fast(__builtin_fmaf(x, kLog2e, -m_log2e));
+}
+
+// ---------------------------------------------------------------------------
+// Combines.  Both are commutative and exact in their comparisons, so a fixed
+// butterfly gives every lane the same bits.
+// ---------------------------------------------------------------------------
+struct MaxSum {
+  float m, s;
+};
+
+__device__ __forceinline__ MaxSum combine(MaxSum a, MaxSum b) {
+  const float m = fmaxf(a.m, b.m);
+  if (m == kNegInf) return {kNegInf, 0.0f};
+  const float ml = m * kLog2e;
+  const float sa = a.s * exp_shift(a.m, ml);
+  const float sb = b.s * exp_shift(b.m, ml);
+  return {m, sa + sb};
+}
+
+struct MaxIdx {
+  float m;
+  int i;
+};
+
+__device__ __forceinline__ MaxIdx combine(MaxIdx a, MaxIdx b) {
+  return (b.m > a.m || (b.m == a.m && b.i < a.i)) ? b : a;
+}
+
+__device__ __forceinline__ MaxSum wave_reduce(MaxSum v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    MaxSum o{__shfl_xor(v.m, off), __shfl_xor(v.s, off)};
+    v = combine(v, o);
+  }
+  return v;
+}
+
+__device__ __forceinline__ MaxIdx wave_reduce(MaxIdx v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    MaxIdx o{__shfl_xor(v.m, off), __shfl_xor(v.i, off)};
+    v = combine(v, o);
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x64-10 (Salmon et al., SC'11): two 64x64->128 multiplies per round,
+// Weyl key schedule, 10 rounds.
+// ---------------------------------------------------------------------------
+struct U64x4 {
+  uint64_t c0, c1, c2, c3;
+};
+
+__device__ __forceinline__ U64x4 philox4x64_10(U64x4 c, uint64_t k0, uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(M0, c.c0), lo0 = M0 * c.c0;
+    const uint64_t hi1 = __umul64hi(M1, c.c2), lo1 = M1 * c.c2;
+    c = {hi1 ^ c.c1 ^ k0, lo1, hi0 ^ c.c3 ^ k1, lo0};
+    k0 += W0;
+    k1 += W1;
+  }
+  return c;
+}
+
+// Top 24 bits of a word on the 2^-24 grid: exact in float32.
+__device__ __forceinline__ float uniform24(uint64_t w) {
+  return static_cast<float>(static_cast<uint32_t>(w >> 40)) * 0x1p-24f;
+}
+
+}  // namespace sv

@@ -1,0 +1,88 @@
+// Kernel argument blocks and launchers (host-callable, defined in sv_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sv_plan.h"
+
+namespace sv {
+
+// Rows of one launch of the row-statistics pass.  Sequence b owns rows_t
+// target rows then rows_d draft rows; workgroup (b, j, seg) reduces segment
+// seg of row j.
+struct RowSet {
+  const char *t;
+  int64_t t_stride_bytes;
+  const char *d;
+  int64_t d_stride_bytes;
+  int32_t rows_t, rows_d;
+  const int32_t *window_len;  // window calls: rows past the window are skipped
+  int32_t gamma;
+  int32_t V, S, seg_len;
+  uint64_t dmask[kTreeMaxNodes / 64];  // draft row j read iff bit j is set
+};
+
+struct WindowArgs {
+  const char *t;
+  int64_t t_stride_bytes;
+  const char *d;
+  int64_t d_stride_bytes;
+  const int32_t *tokens;
+  const int32_t *window_len;
+  int32_t gamma, V, S;
+  uint64_t seed, tag;
+  const uint64_t *seq_ids;
+  const int64_t *base_pos;
+  const float2 *part;
+  int32_t *n_accepted;
+  int32_t *out_tokens;
+  float *p_draft, *q_draft;
+  SampleJob *jobs;
+};
+
+struct GreedyArgs {
+  const int32_t *tokens;
+  const int32_t *window_len;
+  int32_t gamma, V, S;
+  const float2 *part;
+  int32_t *n_accepted;
+  int32_t *out_tokens;
+};
+
+struct TreeArgs {
+  const char *t;
+  const char *d;
+  int64_t seq_bytes;
+  const int32_t *tokens;
+  int32_t V, S, R, mode;
+  uint64_t seed, tag;
+  const uint64_t *seq_ids;
+  const int64_t *base_pos;
+  const float2 *part;
+  int32_t *n_accepted, *best_node, *out_tokens, *out_nodes;
+  SampleJob *jobs;
+  TreeMeta meta;
+};
+
+struct RollbackArgs {
+  int32_t *buf_tokens;
+  int32_t *buf_len;
+  int32_t K, cap;
+  const int32_t *verified;
+  int64_t verified_stride;
+  const int32_t *verified_len;
+  int32_t len_offset;
+};
+
+void launch_row_stats(int dtype, bool argmax, const RowSet &rs, int64_t blocks, float2 *part, hipStream_t st);
+void launch_window_decide(int dtype, const WindowArgs &A, int B, hipStream_t st);
+void launch_greedy_decide(const GreedyArgs &A, int B, hipStream_t st);
+void launch_tree_decide(int dtype, const TreeArgs &A, int B, hipStream_t st);
+void launch_sample(int dtype, const SampleJob *jobs, int B, int V, int C, float *spart, hipStream_t st);
+void launch_rollback(const RollbackArgs &A, int S, int stage, hipStream_t st);
+int probe_blocks(size_t bytes);
+void launch_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t st);
+
+}  // namespace sv
