@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Throughput of speculative-decoding window verification on one MI355X.
+
+Workload (one step = one sv_verify_window call, the whole hot path: row
+statistics, accept test, first rejection, Philox uniforms, residual/bonus
+draw): B=256 sequences, gamma=8 drafts, vocabulary 128256, bf16 logits;
+target N(0, 3^2) plus 6 on one random token per row, draft = target + noise
+with the noise set for per-token acceptance alpha in {0.05, 0.3, 0.6, 0.9}.
+The four alpha batches (4 x 1.116 GB) are distinct buffers used in turn, so
+no step finds its inputs in the 256 MB Infinity Cache.  Inputs are resident
+in HBM before the timed region starts.
+
+Printed: one JSON line.  value = verified draft tokens/s = B * gamma / step
+time.  roofline = the row-statistics kernel (the call's HBM stream): its
+algorithmic bytes B * (2 gamma + 1) * V * 2 per launch over its average
+launch time, measured with HIP events on the stream it runs on.
+cpu_baseline = the float64 oracle on a bounded sample of the same sequences,
+timed on this host.  Smaller workloads (greedy, tree, hierarchy, latency
+configs) are timed in the same run and reported under "also".
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+B, GAMMA, V = 256, 8, 128256
+ALPHAS = (0.05, 0.3, 0.6, 0.9)
+HBM_PEAK_GBPS = 8000.0
+METRIC = "verified draft tokens/s + achieved HBM GB/s, γ=8 window, vocab 128256 bf16"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the oracle timing on the host (baseline only)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-also", action="store_true", help="skip the smaller side workloads")
+    return ap.parse_args()
+
+
+def event_time_ms(torch, fn, reps):
+    """Average duration of fn() over reps launches, HIP events around each."""
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(s)
+        fn()
+        b.record(s)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / reps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(sequences are independent: a batch shards across GPUs with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import draft_token_verification_06_amd as sv
+    from draft_token_verification_06_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    data = [synth.window_config5(a, B=B, seed=1005 + k, device=dev) for k, a in enumerate(ALPHAS)]
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    ws = [sv.workspace(sv.SV_OP_WINDOW, B, GAMMA, V, torch.bfloat16, dev) for _ in ALPHAS]
+    outs = [sv.WindowResult(torch.empty(B, dtype=torch.int32, device=dev),
+                            torch.empty(B, GAMMA + 1, dtype=torch.int32, device=dev),
+                            torch.empty(B, GAMMA, dtype=torch.float32, device=dev),
+                            torch.empty(B, GAMMA, dtype=torch.float32, device=dev))
+            for _ in ALPHAS]
+
+    def step(k, part=None):
+        a = k % len(ALPHAS)
+        d = data[a]
+        sv.verify_window(d["target"], d["draft"], d["tokens"], seed=0, ws=ws[a], out=outs[a],
+                         part=part)
+
+    # untimed reference call per alpha: its outputs are kept for the parity check
+    for k in range(len(ALPHAS)):
+        step(k)
+    torch.cuda.synchronize()
+    ref = [(o.n_accepted.cpu().numpy().copy(), o.out_tokens.cpu().numpy().copy(),
+            o.p_draft.cpu().numpy().copy()) for o in outs]
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # dominant kernel alone: row statistics, HIP events on its stream
+    reps = max(len(ALPHAS), args.steps)
+    rs_ms = event_time_ms(torch, lambda it=iter(range(10 ** 9)): step(next(it), sv.api.SV_PART_ROW_STATS), reps)
+    ds_ms = event_time_ms(torch, lambda it=iter(range(10 ** 9)): step(next(it), sv.api.SV_PART_DECIDE_SAMPLE), reps)
+    full_ms = event_time_ms(torch, lambda it=iter(range(10 ** 9)): step(next(it)), reps)
+    alg_bytes = B * (2 * GAMMA + 1) * V * 2
+    rs_gbps = alg_bytes / (rs_ms * 1e-3) / 1e9
+    step_gbps = alg_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # read ceiling of this GPU through the same 16-byte loads (2 GiB, beyond the MALL)
+    probe_buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    probe_buf.fill_(1)
+    sink = sv.probe_read(probe_buf)
+    probe_ms = event_time_ms(torch, lambda: sv.probe_read(probe_buf, sink), 20)
+    probe_gbps = probe_buf.numel() / (probe_ms * 1e-3) / 1e9
+    del probe_buf
+    # a plain copy of known size (1 GiB), for scaling hardware byte counters
+    cp_src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    cp_dst.copy_(cp_src)
+    torch.cuda.synchronize()
+    del cp_src, cp_dst
+
+    line = {
+        "metric": METRIC,
+        "value": B * GAMMA / (ms_per_step * 1e-3),
+        "unit": "verified draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "stochastic window verify, B=256, gamma=8, V=128256, bf16 logits; "
+                        "draft noise for alpha 0.05/0.3/0.6/0.9, the four batches used in turn",
+            "B": B, "gamma": GAMMA, "V": V, "alphas": list(ALPHAS),
+            "input_bytes_per_step": alg_bytes,
+        },
+        "achieved_GBps_step": step_gbps,
+        "frac_of_hbm_peak_step": step_gbps / HBM_PEAK_GBPS,
+        "roofline": {
+            "kernel": "k_row_stats<bf16> (row statistics)",
+            "bound": "hbm",
+            "achieved": rs_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": rs_gbps / HBM_PEAK_GBPS,
+            "traffic": None,
+            "avg_launch_us": rs_ms * 1e3,
+            "bytes_per_launch": alg_bytes,
+            "frac_of_probe_read": rs_gbps / probe_gbps,
+        },
+        "breakdown_us": {"row_stats": rs_ms * 1e3, "decide_sample": ds_ms * 1e3,
+                         "full_call_events": full_ms * 1e3},
+        "probe_read_GBps": probe_gbps,
+        "bytes_per_verified_draft": alg_bytes / (B * GAMMA),
+        "gen_seconds": t_gen,
+    }
+
+    # mean emitted tokens per window against the closed form (1-a^(g+1))/(1-a)
+    acc = {}
+    for a, (n, _, _) in zip(ALPHAS, ref):
+        acc[str(a)] = {"mean_emitted": float((n + 1).mean()),
+                       "closed_form_nominal_alpha": (1 - a ** (GAMMA + 1)) / (1 - a)}
+    line["emitted_per_window"] = acc
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"], line["parity_sample"] = cpu_baseline(data, ref, args.cpu_seconds)
+        for a, st in zip(ALPHAS, line["parity_sample"].pop("beta", [])):
+            acc[str(a)]["closed_form_sample_rows"] = st
+    if not args.no_also:
+        line["also"] = side_workloads(torch, sv, synth, dev)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(data, ref, budget_s):
+    """Float64 oracle on sequences taken round-robin over the four alpha
+    batches until the time budget is spent; also checks the GPU's reference
+    outputs on those sequences (tolerance and margin rule of the tests)."""
+    import numpy as np
+    import oracle
+    from draft_token_verification_06_amd.synth import to_host_bits
+
+    done, margins, mismatches = 0, 0, 0
+    beta_rows = [[] for _ in ALPHAS]
+    per_alpha = [[] for _ in ALPHAS]
+    wall = 0.0
+    b = 0
+    while wall < budget_s and b < B:
+        for a in range(len(ALPHAS)):
+            d = data[a]
+            T = oracle.decode(to_host_bits(d["target"][b]), "bf16")
+            D = oracle.decode(to_host_bits(d["draft"][b]), "bf16")
+            toks = d["tokens"][b].cpu().numpy()
+            t0 = time.perf_counter()
+            u, v = oracle.window_uniforms(0, 0, b, 0, GAMMA)
+            o = oracle.verify_window(T, D, toks, GAMMA, u, v)
+            wall += time.perf_counter() - t0
+            done += 1
+            n, out, P = ref[a][0][b], ref[a][1][b], ref[a][2][b]
+            want = o["out"] + [-1] * (GAMMA + 1 - len(o["out"]))
+            ok_p = all(abs(P[i] - o["P"][i]) <= 1e-5 * o["P"][i] for i in range(min(o["n"] + 1, GAMMA)))
+            if n == o["n"] and list(out) == want and ok_p:
+                pass
+            else:
+                margin = any(np.isfinite(r) and abs(o["u"][i] - r) < 1e-5 for i, r in enumerate(o["ratio"]))
+                s = o["sample"]
+                margin |= abs(s["tau"] - s["C_lo"]) / s["Z"] < 1e-5 or abs(s["tau"] - s["C_hi"]) / s["Z"] < 1e-5
+                if margin and ok_p:
+                    margins += 1
+                else:
+                    mismatches += 1
+            # exact expected emitted count of this window from its own rows
+            betas = [float(np.minimum(oracle.softmax(T[i]), oracle.softmax(D[i])).sum()) for i in range(GAMMA)]
+            e, pr = 1.0, 1.0
+            for i in range(GAMMA):
+                pr *= betas[i]
+                e += pr
+            beta_rows[a].append(e)
+            per_alpha[a].append(float(np.mean(betas)))
+        b += 1
+    value = done * GAMMA / wall
+    base = {"value": value, "unit": "verified draft tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} sequences (round-robin over the 4 alpha batches) of the B=256 gamma=8 "
+                      f"V=128256 bf16 workload, float64 oracle, one process, {wall:.1f} s",
+            "seconds": wall}
+    parity = {"sequences": done, "margin_cases": margins, "mismatches": mismatches,
+              "beta": [{"exact_expected_emitted": float(np.mean(x)), "mean_alpha": float(np.mean(y))}
+                       for x, y in zip(beta_rows, per_alpha)]}
+    return base, parity
+
+
+def side_workloads(torch, sv, synth, dev):
+    """Latency-bound configurations and the other entry points, same run."""
+    out = {}
+    reps = 50
+
+    # greedy on the same B=256 gamma=8 target rows
+    d = synth.window_config5(0.6, B=B, seed=2005, device=dev)
+    wsg = sv.workspace(sv.SV_OP_GREEDY, B, GAMMA, V, torch.bfloat16, dev)
+    g_ms = event_time_ms(torch, lambda: sv.verify_greedy(d["target"], d["tokens"], ws=wsg), reps)
+    gbytes = B * (GAMMA + 1) * V * 2
+    out["greedy_B256_g8_V128256_bf16"] = {"us": g_ms * 1e3, "GBps": gbytes / (g_ms * 1e-3) / 1e9,
+                                          "verified_drafts_per_s": B * GAMMA / (g_ms * 1e-3)}
+    del d, wsg
+
+    # B=8 gamma=8 bf16 (latency regime), B=1 gamma=4 fp32
+    for name, d in (("window_B8_g8_V128256_bf16", synth.window_batch(8, 8, 128256, "bf16", 3.0, 6.0, 1.0, seed=1002, device=dev)),
+                    ("window_B1_g4_V32000_f32", synth.window_config1(device=dev))):
+        Bx, g = d["tokens"].shape
+        w = sv.workspace(sv.SV_OP_WINDOW, Bx, g, d["V"], d["target"].dtype, dev)
+        ms = event_time_ms(torch, lambda: sv.verify_window(d["target"], d["draft"], d["tokens"], ws=w), reps)
+        nbytes = Bx * (2 * g + 1) * d["V"] * d["target"].element_size()
+        out[name] = {"us": ms * 1e3, "GBps": nbytes / (ms * 1e-3) / 1e9}
+
+    # tree (4, 3, 2), B=4, V=50257 fp16
+    d = synth.tree_config3(device=dev)
+    w = sv.workspace(sv.SV_OP_TREE, 4, 41, 50257, torch.float16, dev)
+    for mode in ("greedy", "stochastic"):
+        ms = event_time_ms(torch, lambda: sv.verify_tree(d["target"], d["draft"], d["tokens"], d["parent"],
+                                                         mode=mode, ws=w), reps)
+        out[f"tree_432_B4_V50257_f16_{mode}"] = {"us": ms * 1e3}
+
+    # PipeSpec-shaped hierarchy, 64 streams: stage-1 window, rollback, stage-2 window, rollback
+    h = synth.hierarchy_config4(S=64, mode="stochastic", device=dev)
+    S = 64
+    bt = torch.zeros(S, 3, 16, dtype=torch.int32, device=dev)
+    bl = torch.zeros(S, 3, dtype=torch.int32, device=dev)
+    w1 = sv.workspace(sv.SV_OP_WINDOW, S, 8, V, torch.bfloat16, dev)
+    w2 = sv.workspace(sv.SV_OP_WINDOW, S, 4, V, torch.bfloat16, dev)
+    r1 = sv.verify_window(h["S1"], h["S0"], h["o0"], tag=1, ws=w1)
+    wl2 = torch.clamp(r1.n_accepted + 1, max=4).to(torch.int32)
+    toks2 = r1.out_tokens[:, :4].contiguous()
+    s1_ms = event_time_ms(torch, lambda: sv.verify_window(h["S1"], h["S0"], h["o0"], tag=1, ws=w1, out=r1), reps)
+    r2 = sv.verify_window(h["F"][:, :5], h["S1"][:, :4], toks2, tag=2, window_len=wl2, ws=w2)
+    s2_ms = event_time_ms(torch, lambda: sv.verify_window(h["F"][:, :5], h["S1"][:, :4], toks2, tag=2,
+                                                          window_len=wl2, ws=w2, out=r2), reps)
+    rb_ms = event_time_ms(torch, lambda: sv.rollback(bt, bl, 2, r2.out_tokens, r2.n_accepted, len_offset=1), reps)
+    out["hierarchy_64_streams_V128256_bf16"] = {
+        "stage1_us": s1_ms * 1e3, "stage1_GBps": S * 17 * V * 2 / (s1_ms * 1e-3) / 1e9,
+        "stage2_us": s2_ms * 1e3, "rollback_us": rb_ms * 1e3}
+    return out
+
+
+if __name__ == "__main__":
+    main()

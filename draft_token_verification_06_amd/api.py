@@ -89,9 +89,13 @@ class TreeResult:
     out_nodes: torch.Tensor
 
 
+SV_PART_ROW_STATS, SV_PART_DECIDE_SAMPLE = 1, 2
+
+
 def verify_window(target, draft, tokens, *, seed=0, tag=0, window_len=None, seq_ids=None,
-                  base_pos=None, return_probs=False, ws=None, out=None):
-    """Stochastic window verification: sv_verify_window."""
+                  base_pos=None, return_probs=False, ws=None, out=None, part=None):
+    """Stochastic window verification: sv_verify_window, or one half of it
+    (sv_verify_window_part) when part is SV_PART_ROW_STATS / SV_PART_DECIDE_SAMPLE."""
     B, rows, V = target.shape
     gamma = rows - 1
     ts = _logits(target, gamma + 1, "target")
@@ -111,9 +115,10 @@ def verify_window(target, draft, tokens, *, seed=0, tag=0, window_len=None, seq_
         if return_probs:
             out.p_draft = torch.empty(B, gamma, dtype=torch.float32, device=dev)
             out.q_draft = torch.empty(B, gamma, dtype=torch.float32, device=dev)
+    head = (lib().sv_verify_window,) if part is None else (lib().sv_verify_window_part, part)
     with torch.cuda.device(dev):
-        _check(lib().sv_verify_window(
-            _ptr(target), ts, _ptr(draft), ds, _DTYPE_CODE[target.dtype],
+        _check(head[0](
+            *head[1:], _ptr(target), ts, _ptr(draft), ds, _DTYPE_CODE[target.dtype],
             _ptr(tokens), _ptr(window_len), B, gamma, V,
             ctypes.c_uint64(seed), ctypes.c_uint64(tag), _ptr(seq_ids), _ptr(base_pos),
             _ptr(out.n_accepted), _ptr(out.out_tokens), _ptr(out.p_draft), _ptr(out.q_draft),

@@ -4,7 +4,7 @@
 #include <cstdint>
 #include <cstring>
 
-#include "../../include/sv.h"
+#include "sv.h"
 #include "sv_launch.h"
 #include "sv_plan.h"
 
@@ -29,6 +29,11 @@ int check_workspace(void *ws, size_t bytes, size_t need) {
   if (need == 0) return SV_EINVAL;
   if (!ws || !aligned(ws, 256) || bytes < need) return SV_EWORKSPACE;
   return SV_OK;
+}
+
+// Row-statistics grids are one-dimensional with 32-bit block indices.
+bool grid_fits(int64_t B, const Layout &L) {
+  return B * L.rows_per_seq * L.plan.S < (int64_t(1) << 31);
 }
 
 int launch_status() {
@@ -80,7 +85,7 @@ const char *sv_strerror(int status) {
 }
 
 size_t sv_workspace_size(int op, int32_t B, int32_t n, int32_t V, int dtype) {
-  if (elem_bytes(dtype) == 0 || B < 1 || V < 1) return 0;
+  if (elem_bytes(dtype) == 0 || B < 1 || V < 1 || V > kMaxVocab) return 0;
   if (op == SV_OP_WINDOW || op == SV_OP_GREEDY) {
     if (n < 1 || n > SV_MAX_GAMMA) return 0;
   } else if (op == SV_OP_TREE) {
@@ -91,18 +96,23 @@ size_t sv_workspace_size(int op, int32_t B, int32_t n, int32_t V, int dtype) {
   return make_layout(op, B, n, V).total;
 }
 
-int sv_verify_window(const void *target_logits, int64_t target_seq_stride,
-                     const void *draft_logits, int64_t draft_seq_stride, int dtype,
-                     const int32_t *draft_tokens, const int32_t *window_len,
-                     int32_t B, int32_t gamma, int32_t V,
-                     uint64_t seed, uint64_t tag, const uint64_t *seq_ids,
-                     const int64_t *base_pos,
-                     int32_t *n_accepted, int32_t *out_tokens,
-                     float *p_draft, float *q_draft,
-                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// parts: bit 0 = row statistics, bit 1 = decide + sampling.
+int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
+                const void *draft_logits, int64_t draft_seq_stride, int dtype,
+                const int32_t *draft_tokens, const int32_t *window_len,
+                int32_t B, int32_t gamma, int32_t V,
+                uint64_t seed, uint64_t tag, const uint64_t *seq_ids,
+                const int64_t *base_pos,
+                int32_t *n_accepted, int32_t *out_tokens,
+                float *p_draft, float *q_draft,
+                void *workspace, size_t workspace_bytes, hipStream_t stream) {
   const int eb = elem_bytes(dtype);
   if (eb == 0) return SV_EDTYPE;
-  if (B < 1 || gamma < 1 || gamma > SV_MAX_GAMMA || V < 1) return SV_EINVAL;
+  if (B < 1 || gamma < 1 || gamma > SV_MAX_GAMMA || V < 1 || V > kMaxVocab) return SV_EINVAL;
   if (!target_logits || !draft_logits || !draft_tokens || !n_accepted || !out_tokens) return SV_EINVAL;
   if (!aligned(target_logits, eb) || !aligned(draft_logits, eb)) return SV_EINVAL;
   const int64_t t_rows = static_cast<int64_t>(gamma + 1) * V;
@@ -111,13 +121,13 @@ int sv_verify_window(const void *target_logits, int64_t target_seq_stride,
   if (draft_seq_stride == 0) draft_seq_stride = d_rows;
   if (target_seq_stride < t_rows || draft_seq_stride < d_rows) return SV_EINVAL;
   const Layout L = make_layout(SV_OP_WINDOW, B, gamma, V);
+  if (!grid_fits(B, L)) return SV_EINVAL;
   const int ws = check_workspace(workspace, workspace_bytes, L.total);
   if (ws != SV_OK) return ws;
 
   char *wsb = static_cast<char *>(workspace);
   float2 *part = reinterpret_cast<float2 *>(wsb + L.part_off);
   SampleJob *jobs = reinterpret_cast<SampleJob *>(wsb + L.jobs_off);
-  float *spart = reinterpret_cast<float *>(wsb + L.spart_off);
 
   RowSet rs{};
   rs.t = static_cast<const char *>(target_logits);
@@ -132,7 +142,9 @@ int sv_verify_window(const void *target_logits, int64_t target_seq_stride,
   rs.S = L.plan.S;
   rs.seg_len = L.plan.seg_len;
   for (auto &m : rs.dmask) m = ~0ull;
-  launch_row_stats(dtype, false, rs, static_cast<int64_t>(B) * L.rows_per_seq * L.plan.S, part, stream);
+  if (parts & 1)
+    launch_row_stats(dtype, false, rs, static_cast<int64_t>(B) * L.rows_per_seq * L.plan.S, part, stream);
+  if (!(parts & 2)) return launch_status();
 
   WindowArgs A{};
   A.t = rs.t;
@@ -154,9 +166,42 @@ int sv_verify_window(const void *target_logits, int64_t target_seq_stride,
   A.p_draft = p_draft;
   A.q_draft = q_draft;
   A.jobs = jobs;
-  launch_window_decide(dtype, A, B, stream);
-  launch_sample(dtype, jobs, B, V, L.chunks, spart, stream);
+  launch_window_finish(dtype, A, B, stream);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sv_verify_window(const void *target_logits, int64_t target_seq_stride,
+                     const void *draft_logits, int64_t draft_seq_stride, int dtype,
+                     const int32_t *draft_tokens, const int32_t *window_len,
+                     int32_t B, int32_t gamma, int32_t V,
+                     uint64_t seed, uint64_t tag, const uint64_t *seq_ids,
+                     const int64_t *base_pos,
+                     int32_t *n_accepted, int32_t *out_tokens,
+                     float *p_draft, float *q_draft,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return window_impl(3, target_logits, target_seq_stride, draft_logits, draft_seq_stride, dtype,
+                     draft_tokens, window_len, B, gamma, V, seed, tag, seq_ids, base_pos,
+                     n_accepted, out_tokens, p_draft, q_draft, workspace, workspace_bytes, stream);
+}
+
+int sv_verify_window_part(int part, const void *target_logits, int64_t target_seq_stride,
+                          const void *draft_logits, int64_t draft_seq_stride, int dtype,
+                          const int32_t *draft_tokens, const int32_t *window_len,
+                          int32_t B, int32_t gamma, int32_t V,
+                          uint64_t seed, uint64_t tag, const uint64_t *seq_ids,
+                          const int64_t *base_pos,
+                          int32_t *n_accepted, int32_t *out_tokens,
+                          float *p_draft, float *q_draft,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (part != SV_PART_ROW_STATS && part != SV_PART_DECIDE_SAMPLE) return SV_EINVAL;
+  return window_impl(part == SV_PART_ROW_STATS ? 1 : 2, target_logits, target_seq_stride,
+                     draft_logits, draft_seq_stride, dtype, draft_tokens, window_len, B, gamma, V,
+                     seed, tag, seq_ids, base_pos, n_accepted, out_tokens, p_draft, q_draft,
+                     workspace, workspace_bytes, stream);
 }
 
 int sv_verify_greedy(const void *target_logits, int64_t target_seq_stride, int dtype,
@@ -166,13 +211,14 @@ int sv_verify_greedy(const void *target_logits, int64_t target_seq_stride, int d
                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
   const int eb = elem_bytes(dtype);
   if (eb == 0) return SV_EDTYPE;
-  if (B < 1 || gamma < 1 || gamma > SV_MAX_GAMMA || V < 1) return SV_EINVAL;
+  if (B < 1 || gamma < 1 || gamma > SV_MAX_GAMMA || V < 1 || V > kMaxVocab) return SV_EINVAL;
   if (!target_logits || !draft_tokens || !n_accepted || !out_tokens) return SV_EINVAL;
   if (!aligned(target_logits, eb)) return SV_EINVAL;
   const int64_t t_rows = static_cast<int64_t>(gamma + 1) * V;
   if (target_seq_stride == 0) target_seq_stride = t_rows;
   if (target_seq_stride < t_rows) return SV_EINVAL;
   const Layout L = make_layout(SV_OP_GREEDY, B, gamma, V);
+  if (!grid_fits(B, L)) return SV_EINVAL;
   const int ws = check_workspace(workspace, workspace_bytes, L.total);
   if (ws != SV_OK) return ws;
   float2 *part = reinterpret_cast<float2 *>(static_cast<char *>(workspace) + L.part_off);
@@ -219,7 +265,7 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
   const int eb = elem_bytes(dtype);
   if (eb == 0) return SV_EDTYPE;
-  if (B < 1 || V < 1 || (mode != SV_TREE_GREEDY && mode != SV_TREE_STOCHASTIC)) return SV_EINVAL;
+  if (B < 1 || V < 1 || V > kMaxVocab || (mode != SV_TREE_GREEDY && mode != SV_TREE_STOCHASTIC)) return SV_EINVAL;
   TreeMeta meta;
   const int tst = build_tree(parent_host, N, &meta);
   if (tst != SV_OK) return tst;
@@ -228,12 +274,12 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
   if (mode == SV_TREE_STOCHASTIC && !draft_logits) return SV_EINVAL;
   if (!aligned(target_logits, eb) || (draft_logits && !aligned(draft_logits, eb))) return SV_EINVAL;
   const Layout L = make_layout(SV_OP_TREE, B, N, V);
+  if (!grid_fits(B, L)) return SV_EINVAL;
   const int ws = check_workspace(workspace, workspace_bytes, L.total);
   if (ws != SV_OK) return ws;
   char *wsb = static_cast<char *>(workspace);
   float2 *part = reinterpret_cast<float2 *>(wsb + L.part_off);
   SampleJob *jobs = reinterpret_cast<SampleJob *>(wsb + L.jobs_off);
-  float *spart = reinterpret_cast<float *>(wsb + L.spart_off);
 
   const int64_t seq_bytes = static_cast<int64_t>(N) * V * eb;
   RowSet rs{};
@@ -282,7 +328,7 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
   A.jobs = jobs;
   A.meta = meta;
   launch_tree_decide(dtype, A, B, stream);
-  if (mode == SV_TREE_STOCHASTIC) launch_sample(dtype, jobs, B, V, L.chunks, spart, stream);
+  if (mode == SV_TREE_STOCHASTIC) launch_tree_finish(dtype, jobs, B, V, stream);
   return launch_status();
 }
 

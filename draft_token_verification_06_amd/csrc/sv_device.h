@@ -15,6 +15,31 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 
+// Pointers known to address global memory (address space 1): loads through
+// them compile to global_load rather than flat_load, also when the pointer
+// value was read from LDS.
+#define SV_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const SV_GLOBAL T *as_global(const T *p) {
+  return reinterpret_cast<const SV_GLOBAL T *>(reinterpret_cast<uintptr_t>(p));
+}
+template <typename T>
+__device__ __forceinline__ const SV_GLOBAL T *as_global(const void *p) {
+  return reinterpret_cast<const SV_GLOBAL T *>(reinterpret_cast<uintptr_t>(p));
+}
+
+// 16-byte streaming load with the nontemporal hint: logits are read once per
+// pass, and the hint lifts sustained HBM read bandwidth on gfx950.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
+  const u32x4_t v = __builtin_nontemporal_load(as_global<u32x4_t>(static_cast<const void *>(p)));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 load_vec(const void *p) {
+  const u32x4_t v = *as_global<u32x4_t>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---------------------------------------------------------------------------
 // Logit decoding.  A 16-byte vector holds EPV elements; decoding is exact.
 // ---------------------------------------------------------------------------
@@ -25,7 +50,7 @@ template <> struct Elt<DT_BF16> {
   static constexpr int kEPV = 8;
   static constexpr uint32_t kNegInfPair = 0xFF80FF80u;  // two bf16 -inf
   __device__ static __forceinline__ float one(const void *row, int64_t i) {
-    const uint32_t r = reinterpret_cast<const uint16_t *>(row)[i];
+    const uint32_t r = as_global<uint16_t>(row)[i];
     return __uint_as_float(r << 16);
   }
   __device__ static __forceinline__ void vec(const uint4 &r, float *x) {
@@ -46,7 +71,7 @@ template <> struct Elt<DT_F16> {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
   }
   __device__ static __forceinline__ float one(const void *row, int64_t i) {
-    return h2f(reinterpret_cast<const uint16_t *>(row)[i]);
+    return h2f(as_global<uint16_t>(row)[i]);
   }
   __device__ static __forceinline__ void vec(const uint4 &r, float *x) {
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -63,7 +88,7 @@ template <> struct Elt<DT_F32> {
   static constexpr int kEPV = 4;
   static constexpr uint32_t kNegInfPair = 0xFF800000u;  // one f32 -inf
   __device__ static __forceinline__ float one(const void *row, int64_t i) {
-    return reinterpret_cast<const float *>(row)[i];
+    return as_global<float>(row)[i];
   }
   __device__ static __forceinline__ void vec(const uint4 &r, float *x) {
     x[0] = __uint_as_float(r.x);
@@ -72,6 +97,7 @@ template <> struct Elt<DT_F32> {
     x[3] = __uint_as_float(r.w);
   }
 };
+
 
 // 2^x on the hardware transcendental unit (v_exp_f32).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -90,13 +116,15 @@ struct MaxSum {
   float m, s;
 };
 
+// Rescale factor 2^((from - to) log2e) = exp(from - to) for from <= to.  It is
+// taken from the difference of the two maxima, so the side that already holds
+// the maximum is multiplied by exactly 1 and repeated combines add no bias.
+__device__ __forceinline__ float rescale(float from, float to) { return exp2_fast((from - to) * kLog2e); }
+
 __device__ __forceinline__ MaxSum combine(MaxSum a, MaxSum b) {
   const float m = fmaxf(a.m, b.m);
   if (m == kNegInf) return {kNegInf, 0.0f};
-  const float ml = m * kLog2e;
-  const float sa = a.s * exp_shift(a.m, ml);
-  const float sb = b.s * exp_shift(b.m, ml);
-  return {m, sa + sb};
+  return {m, a.s * rescale(a.m, m) + b.s * rescale(b.m, m)};
 }
 
 struct MaxIdx {

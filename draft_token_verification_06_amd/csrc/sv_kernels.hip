@@ -6,13 +6,14 @@
 //   kUnroll vectors are kept in registers: the batch maximum is taken first so
 //   that every element costs exactly one exponential, then wave butterflies and
 //   one LDS step finish the workgroup in a fixed order.
-// Decide, k_window_decide / k_greedy_decide / k_tree_decide: one wavefront (or
+// Decide (window_decide, k_greedy_decide, k_tree_decide): one wavefront (or
 //   one workgroup for trees) per sequence combines the segment results, forms
 //   p(x) and q(x) at the draft tokens, draws the Philox uniforms, and finds the
 //   first rejection with a wavefront ballot.
-// Sampling, k_sample_partial + k_sample_select: the one extra pass over the
-//   row of the first rejection (or the bonus row): chunk sums of the weights,
-//   then an inverse-CDF search inside the chunk holding tau = v * Z.
+// Sampling (k_finish, one 1024-thread workgroup per sequence): the one extra
+//   pass over the row of the first rejection (or the bonus row) keeps chunk
+//   sums of the weights in LDS, then searches the chunk holding tau = v * Z.
+//   For windows the decide runs in wave 0 of the same workgroup.
 // Rollback, k_rollback: first divergence by ballot, then copy of the
 //   verified tail.
 #include <climits>
@@ -23,7 +24,12 @@
 
 namespace sv {
 
-constexpr int kUnroll = 4;  // 16-byte loads in flight per thread
+#ifndef SV_ROW_UNROLL
+#define SV_ROW_UNROLL 8
+#endif
+// 16-byte loads per thread per batch; the next batch is loaded while the
+// current one is reduced, so 2 * kUnroll loads are in flight per thread.
+constexpr int kUnroll = SV_ROW_UNROLL;
 
 // ---------------------------------------------------------------------------
 // Pass 1: row statistics
@@ -40,7 +46,7 @@ struct RowAcc<DT, false> {
 #pragma unroll
     for (int k = 1; k < kUnroll * Elt<DT>::kEPV; ++k) bm = fmaxf(bm, x[k]);
     if (bm > m) {
-      s *= exp_shift(m, bm * kLog2e);
+      s *= rescale(m, bm);
       m = bm;
     }
     if (m != kNegInf) {
@@ -54,7 +60,7 @@ struct RowAcc<DT, false> {
   }
   __device__ __forceinline__ void one(float x, int) {
     if (x > m) {
-      s = s * exp_shift(m, x * kLog2e) + 1.0f;
+      s = s * rescale(m, x) + 1.0f;
       m = x;
     } else if (m != kNegInf) {
       s += exp_shift(x, m * kLog2e);
@@ -120,10 +126,10 @@ template <int DT, bool kArgmax>
 __global__ void __launch_bounds__(kRowThreads) k_row_stats(RowSet rs, float2 *__restrict__ part) {
   using E = Elt<DT>;
   constexpr int EPV = E::kEPV;
-  const int R = rs.rows_t + rs.rows_d;
-  const int64_t blk = blockIdx.x;
-  const int seg = static_cast<int>(blk % rs.S);
-  const int64_t rj = blk / rs.S;
+  const uint32_t R = rs.rows_t + rs.rows_d;
+  const uint32_t blk = blockIdx.x;  // B * R * S < 2^31 (checked on the host)
+  const int seg = static_cast<int>(blk % static_cast<uint32_t>(rs.S));
+  const uint32_t rj = blk / static_cast<uint32_t>(rs.S);
   const int j = static_cast<int>(rj % R);
   const int64_t b = rj / R;
 
@@ -155,18 +161,43 @@ __global__ void __launch_bounds__(kRowThreads) k_row_stats(RowSet rs, float2 *__
   const int tid = threadIdx.x;
 
   RowAcc<DT, kArgmax> acc;
-  const uint4 neg = make_uint4(E::kNegInfPair, E::kNegInfPair, E::kNegInfPair, E::kNegInfPair);
-  for (int v0 = 0; v0 < nvec; v0 += kUnroll * kRowThreads) {
+  // Full batches: every load in range, no per-lane guards, so the next batch's
+  // loads stay in flight while the current batch is reduced.
+  constexpr int kStep = kUnroll * kRowThreads;
+  const int nfull = nvec / kStep;
+  if (nfull > 0) {
+    uint4 cur[kUnroll], nxt[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) cur[u] = load_stream(vp + u * kRowThreads + tid);
+    for (int it = 0; it < nfull - 1; ++it) {
+      const uint4 *q = vp + (it + 1) * kStep + tid;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) nxt[u] = load_stream(q + u * kRowThreads);
+      float x[kUnroll * EPV];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) E::vec(cur[u], x + u * EPV);
+      acc.batch(x, a + (it * kStep + tid) * EPV, kRowThreads * EPV);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+    }
+    float x[kUnroll * EPV];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) E::vec(cur[u], x + u * EPV);
+    acc.batch(x, a + ((nfull - 1) * kStep + tid) * EPV, kRowThreads * EPV);
+  }
+  // Remainder batch (fewer than kStep vectors), guarded; -inf fills the gaps.
+  if (nfull * kStep < nvec) {
+    const uint4 neg = make_uint4(E::kNegInfPair, E::kNegInfPair, E::kNegInfPair, E::kNegInfPair);
     uint4 r[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int vi = v0 + u * kRowThreads + tid;
-      r[u] = vi < nvec ? vp[vi] : neg;
+      const int vi = nfull * kStep + u * kRowThreads + tid;
+      r[u] = vi < nvec ? load_stream(vp + vi) : neg;
     }
     float x[kUnroll * EPV];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) E::vec(r[u], x + u * EPV);
-    acc.batch(x, a + (v0 + tid) * EPV, kRowThreads * EPV);
+    acc.batch(x, a + (nfull * kStep + tid) * EPV, kRowThreads * EPV);
   }
   for (int k = lo + tid; k < a; k += kRowThreads) acc.one(E::one(row, k), k);
   for (int k = tail + tid; k < hi; k += kRowThreads) acc.one(E::one(row, k), k);
@@ -194,34 +225,39 @@ __device__ __forceinline__ float prob_at(float x, MaxSum st) {
   return exp_shift(x, st.m * kLog2e) / st.s;
 }
 
+// Exponent offset c with p_k = 2^(x_k log2e - c): c = m log2e + log2(s).
+__device__ __forceinline__ float norm_offset(MaxSum st) { return st.m * kLog2e + log2f(st.s); }
+
 // ---------------------------------------------------------------------------
-// Decide: stochastic window
+// Decide: stochastic window (wave 0 of the calling workgroup)
 // ---------------------------------------------------------------------------
+// Lane i examines draft i: p_i(x_i), q_i(x_i) from the row results, the
+// accept uniform of (seq, base_pos + 1 + i), accept iff u * q < p; the first
+// rejection is the first zero of the ballot.  Returns the sampling job of the
+// sequence in *job (JOB_NONE when the sequence is marked invalid).  When
+// `write` is set this workgroup also writes the sequence's outputs.
 template <int DT>
-__global__ void __launch_bounds__(kWave) k_window_decide(WindowArgs A) {
+__device__ void window_decide(const WindowArgs &A, int b, int i, bool write, SampleJob *job) {
   using E = Elt<DT>;
-  const int b = blockIdx.x;
-  const int i = threadIdx.x;
   const int R = 2 * A.gamma + 1;
   int32_t *out = A.out_tokens + static_cast<int64_t>(b) * (A.gamma + 1);
   const int len = A.window_len ? A.window_len[b] : A.gamma;
+  const int xi = i < A.gamma ? A.tokens[static_cast<int64_t>(b) * A.gamma + i] : 0;
   const bool bad_len = len < 0 || len > A.gamma;
-  int x = 0;
-  if (!bad_len && i < len) x = A.tokens[static_cast<int64_t>(b) * A.gamma + i];
-  const bool bad_tok = !bad_len && i < len && (x < 0 || x >= A.V);
+  const bool bad_tok = !bad_len && i < len && (xi < 0 || xi >= A.V);
   if (__any(bad_len || bad_tok)) {
-    for (int k = i; k <= A.gamma; k += kWave) out[k] = -1;
-    if (A.p_draft)
-      for (int k = i; k < A.gamma; k += kWave) A.p_draft[static_cast<int64_t>(b) * A.gamma + k] = 0.0f;
-    if (A.q_draft)
-      for (int k = i; k < A.gamma; k += kWave) A.q_draft[static_cast<int64_t>(b) * A.gamma + k] = 0.0f;
-    if (i == 0) {
-      A.n_accepted[b] = -1;
-      A.jobs[b].mode = JOB_NONE;
+    if (write) {
+      for (int k = i; k <= A.gamma; k += kWave) out[k] = -1;
+      for (int k = i; k < A.gamma; k += kWave) {
+        if (A.p_draft) A.p_draft[static_cast<int64_t>(b) * A.gamma + k] = 0.0f;
+        if (A.q_draft) A.q_draft[static_cast<int64_t>(b) * A.gamma + k] = 0.0f;
+      }
+      if (i == 0) A.n_accepted[b] = -1;
     }
+    if (i == 0) job->mode = JOB_NONE;
     return;
   }
-
+  const int x = i < len ? xi : 0;
   const float2 *prow = A.part + static_cast<int64_t>(b) * R * A.S;
   const char *trow0 = A.t + b * A.t_stride_bytes;
   const char *drow0 = A.d + b * A.d_stride_bytes;
@@ -229,50 +265,59 @@ __global__ void __launch_bounds__(kWave) k_window_decide(WindowArgs A) {
   const uint64_t seq = A.seq_ids ? A.seq_ids[b] : static_cast<uint64_t>(b);
   const int64_t base = A.base_pos ? A.base_pos[b] : 0;
 
-  float P = 0.0f, Q = 0.0f;
+  MaxSum st{0.0f, 1.0f}, sd{0.0f, 1.0f};
+  float P = 0.0f, Q = 0.0f, vi = 0.0f;
   bool acc = false;
-  if (i < len) {
-    const MaxSum st = row_maxsum(prow + i * A.S, A.S);
-    const MaxSum sd = row_maxsum(prow + (A.gamma + 1 + i) * A.S, A.S);
-    P = prob_at(E::one(trow0 + i * row_bytes, x), st);
-    Q = prob_at(E::one(drow0 + i * row_bytes, x), sd);
+  if (i <= len) {  // target row i (row len is the bonus row)
+    st = row_maxsum(prow + i * A.S, A.S);
     const U64x4 w = philox4x64_10({seq, static_cast<uint64_t>(base + 1 + i), 0, 0}, A.seed, A.tag);
-    acc = uniform24(w.c0) * Q < P;
+    vi = uniform24(w.c1);
+    if (i < len) {
+      sd = row_maxsum(prow + (A.gamma + 1 + i) * A.S, A.S);
+      P = prob_at(E::one(trow0 + i * row_bytes, x), st);
+      Q = prob_at(E::one(drow0 + i * row_bytes, x), sd);
+      acc = uniform24(w.c0) * Q < P;
+    }
   }
   const uint64_t inv = ~static_cast<uint64_t>(__ballot(acc));
   int n = inv ? __builtin_ctzll(inv) : kWave;
   n = min(n, len);
 
-  if (i < A.gamma) {
-    const int64_t o = static_cast<int64_t>(b) * A.gamma + i;
-    if (A.p_draft) A.p_draft[o] = P;
-    if (A.q_draft) A.q_draft[o] = Q;
-  }
-  for (int k = i; k <= A.gamma; k += kWave)
-    if (k != n) out[k] = k < n ? x : -1;
-  if (i == 0) {
-    A.n_accepted[b] = n;
-    SampleJob job{};
-    const MaxSum st = row_maxsum(prow + n * A.S, A.S);
-    job.t_row = trow0 + n * row_bytes;
-    job.mt_l2e = st.m * kLog2e;
-    job.inv_st = 1.0f / st.s;
-    if (n < len) {
-      const MaxSum sd = row_maxsum(prow + (A.gamma + 1 + n) * A.S, A.S);
-      job.mode = JOB_RESIDUAL;
-      job.d_row = drow0 + n * row_bytes;
-      job.md_l2e = sd.m * kLog2e;
-      job.inv_sd = 1.0f / sd.s;
-    } else {
-      job.mode = JOB_BONUS;
-      job.d_row = nullptr;
-      job.md_l2e = 0.0f;
-      job.inv_sd = 0.0f;
+  if (write) {
+    if (i < A.gamma) {
+      const int64_t o = static_cast<int64_t>(b) * A.gamma + i;
+      if (A.p_draft) A.p_draft[o] = P;
+      if (A.q_draft) A.q_draft[o] = Q;
     }
-    const U64x4 w = philox4x64_10({seq, static_cast<uint64_t>(base + 1 + n), 0, 0}, A.seed, A.tag);
-    job.v = uniform24(w.c1);
-    job.out_slot = out + n;
-    A.jobs[b] = job;
+    for (int k = i; k <= A.gamma; k += kWave)
+      if (k != n) out[k] = k < n ? x : -1;
+  }
+  // statistics and sampling uniform of row n, from lane n
+  MaxSum tn{__shfl(st.m, n & (kWave - 1)), __shfl(st.s, n & (kWave - 1))};
+  const MaxSum dn{__shfl(sd.m, n & (kWave - 1)), __shfl(sd.s, n & (kWave - 1))};
+  float v = __shfl(vi, n & (kWave - 1));
+  if (i == 0) {
+    if (n >= kWave) {  // gamma = 64 with every draft accepted: row 64 has no lane
+      tn = row_maxsum(prow + n * A.S, A.S);
+      const U64x4 w = philox4x64_10({seq, static_cast<uint64_t>(base + 1 + n), 0, 0}, A.seed, A.tag);
+      v = uniform24(w.c1);
+    }
+    SampleJob jb{};
+    jb.t_row = trow0 + n * row_bytes;
+    jb.ct = norm_offset(tn);
+    if (n < len) {
+      jb.mode = JOB_RESIDUAL;
+      jb.d_row = drow0 + n * row_bytes;
+      jb.cd = norm_offset(dn);
+    } else {
+      jb.mode = JOB_BONUS;
+      jb.d_row = nullptr;
+      jb.cd = 0.0f;
+    }
+    jb.v = v;
+    jb.out_slot = out + n;
+    *job = jb;
+    if (write) A.n_accepted[b] = n;
   }
 }
 
@@ -285,25 +330,27 @@ __global__ void __launch_bounds__(kWave) k_greedy_decide(GreedyArgs A) {
   const int R = A.gamma + 1;
   int32_t *out = A.out_tokens + static_cast<int64_t>(b) * (A.gamma + 1);
   const int len = A.window_len ? A.window_len[b] : A.gamma;
+  const int xi = i < A.gamma ? A.tokens[static_cast<int64_t>(b) * A.gamma + i] : 0;
   const bool bad_len = len < 0 || len > A.gamma;
-  int x = 0;
-  if (!bad_len && i < len) x = A.tokens[static_cast<int64_t>(b) * A.gamma + i];
-  const bool bad_tok = !bad_len && i < len && (x < 0 || x >= A.V);
+  const bool bad_tok = !bad_len && i < len && (xi < 0 || xi >= A.V);
   if (__any(bad_len || bad_tok)) {
     for (int k = i; k <= A.gamma; k += kWave) out[k] = -1;
     if (i == 0) A.n_accepted[b] = -1;
     return;
   }
+  const int x = i < len ? xi : 0;
   const float2 *prow = A.part + static_cast<int64_t>(b) * R * A.S;
-  bool mismatch = false;
-  if (i < len) mismatch = x != row_argmax(prow + i * A.S, A.S).i;
-  const uint64_t mask = __ballot(mismatch);
+  int am = 0;
+  if (i <= len) am = row_argmax(prow + i * A.S, A.S).i;
+  const uint64_t mask = __ballot(i < len && x != am);
   const int n = mask ? __builtin_ctzll(mask) : len;
+  int y = __shfl(am, n & (kWave - 1));
   for (int k = i; k <= A.gamma; k += kWave)
     if (k != n) out[k] = k < n ? x : -1;
   if (i == 0) {
+    if (n >= kWave) y = row_argmax(prow + n * A.S, A.S).i;
     A.n_accepted[b] = n;
-    out[n] = row_argmax(prow + n * A.S, A.S).i;
+    out[n] = y;
   }
 }
 
@@ -389,21 +436,16 @@ __global__ void __launch_bounds__(kTreeMaxNodes) k_tree_decide(TreeArgs A) {
       out_t[nd] = row_argmax(prow + best * A.S, A.S).i;
     } else {
       SampleJob job{};
-      const MaxSum st = row_maxsum(prow + best * A.S, A.S);
       job.t_row = t0 + best * row_bytes;
-      job.mt_l2e = st.m * kLog2e;
-      job.inv_st = 1.0f / st.s;
+      job.ct = norm_offset(row_maxsum(prow + best * A.S, A.S));
       if ((A.meta.internal[best >> 6] >> (best & 63)) & 1ull) {
-        const MaxSum sd = row_maxsum(prow + (N + best) * A.S, A.S);
         job.mode = JOB_RESIDUAL;
         job.d_row = d0 + best * row_bytes;
-        job.md_l2e = sd.m * kLog2e;
-        job.inv_sd = 1.0f / sd.s;
+        job.cd = norm_offset(row_maxsum(prow + (N + best) * A.S, A.S));
       } else {
         job.mode = JOB_BONUS;
         job.d_row = nullptr;
-        job.md_l2e = 0.0f;
-        job.inv_sd = 0.0f;
+        job.cd = 0.0f;
       }
       const U64x4 r = philox4x64_10(
           {seq, static_cast<uint64_t>(base + nd + 1), static_cast<uint64_t>(A.meta.rank[best]), 0},
@@ -416,62 +458,159 @@ __global__ void __launch_bounds__(kTreeMaxNodes) k_tree_decide(TreeArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-// Sampling pass
+// Sampling pass: one 1024-thread workgroup per sequence
 // ---------------------------------------------------------------------------
-template <int DT>
-__device__ __forceinline__ float sample_weight(const SampleJob &job, int k) {
-  using E = Elt<DT>;
-  const float p = exp_shift(E::one(job.t_row, k), job.mt_l2e) * job.inv_st;
+// Weight of token k: p_k (bonus) or max(0, p_k - q_k) (residual), with
+// p_k = 2^(t_k log2e - ct), q_k = 2^(d_k log2e - cd).
+// p_k, q_k <= 1, so max(0, p - q) is p - q clamped to [0, 1] (one instruction).
+__device__ __forceinline__ float weight_of(const SampleJob &job, float t, float d) {
+  const float p = exp2_fast(__builtin_fmaf(t, kLog2e, -job.ct));
   if (job.mode != JOB_RESIDUAL) return p;
-  const float q = exp_shift(E::one(job.d_row, k), job.md_l2e) * job.inv_sd;
-  return fmaxf(0.0f, p - q);
+  return __builtin_amdgcn_fmed3f(p - exp2_fast(__builtin_fmaf(d, kLog2e, -job.cd)), 0.0f, 1.0f);
 }
 
-template <int DT>
-__global__ void __launch_bounds__(kSampleThreads) k_sample_partial(const SampleJob *__restrict__ jobs,
-                                                                   int V, int C, float *__restrict__ spart) {
-  const int c = blockIdx.x;
-  const int b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const SampleJob job = jobs[b];
-  float acc = 0.0f;
-  if (job.mode != JOB_NONE) {
-    const int lo = c * kSampleChunk;
-    const int hi = min(V, lo + kSampleChunk);
-    for (int k = lo + tid; k < hi; k += kSampleThreads) acc += sample_weight<DT>(job, k);
+// Both rows of the job start on a 16-byte boundary.
+__device__ __forceinline__ bool job_rows_aligned(const SampleJob &job) {
+  const bool ta = (reinterpret_cast<uintptr_t>(job.t_row) & 15) == 0;
+  const bool da = job.mode != JOB_RESIDUAL || (reinterpret_cast<uintptr_t>(job.d_row) & 15) == 0;
+  return ta && da;
+}
+
+// The row is cut into chunks of kFinThreads * E elements; thread t owns the E
+// contiguous elements [c*CH + t*E, c*CH + (t+1)*E) of chunk c (E = 8 bf16/f16
+// or 4 f32 with 16-byte loads, E = 4 with element loads for unaligned rows),
+// so one chunk is one coalesced sweep of the workgroup.
+template <int DT, bool kVec>
+struct FinGeom {
+  static constexpr int E = kVec ? Elt<DT>::kEPV : 4;
+  static constexpr int CH = kFinThreads * E;
+};
+
+// Weights of thread tid's elements of chunk c (0 past V).
+template <int DT, bool kVec>
+__device__ __forceinline__ void thread_weights(const SampleJob &job, int V, int c, int tid, float *w) {
+  using E = Elt<DT>;
+  using G = FinGeom<DT, kVec>;
+  const int k0 = c * G::CH + tid * G::E;
+  const bool resid = job.mode == JOB_RESIDUAL;
+  if (kVec && k0 + G::E <= V) {
+    const int64_t vi = k0 / G::E;
+    const uint4 rt = load_vec(static_cast<const uint4 *>(job.t_row) + vi);
+    const uint4 rd = resid ? load_vec(static_cast<const uint4 *>(job.d_row) + vi) : make_uint4(0, 0, 0, 0);
+    float xt[Elt<DT>::kEPV], xd[Elt<DT>::kEPV];
+    E::vec(rt, xt);
+    E::vec(rd, xd);
+#pragma unroll
+    for (int e = 0; e < G::E; ++e) w[e] = weight_of(job, xt[e], xd[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < G::E; ++e) {
+      const int k = k0 + e;
+      w[e] = k < V ? weight_of(job, E::one(job.t_row, k), resid ? E::one(job.d_row, k) : 0.0f) : 0.0f;
+    }
   }
-  acc = wave_sum(acc);
-  __shared__ float lds[kSampleThreads / kWave];
-  if ((tid & (kWave - 1)) == 0) lds[tid / kWave] = acc;
+}
+
+// Sum of thread tid's weights of chunk c, then the wave sum into wp.
+template <int DT, bool kVec>
+__device__ __forceinline__ void chunk_sum_guarded(const SampleJob &job, int V, int c, float *wp, int tid) {
+  using G = FinGeom<DT, kVec>;
+  float w[G::E];
+  thread_weights<DT, kVec>(job, V, c, tid, w);
+  float t = 0.0f;
+#pragma unroll
+  for (int e = 0; e < G::E; ++e) t += w[e];
+  t = wave_sum(t);
+  if ((tid & (kWave - 1)) == 0) wp[c * kFinWaves + tid / kWave] = t;
+}
+
+// Weights of kFinBatch chunks already loaded as 16-byte vectors; wave sums to wp.
+template <int DT>
+__device__ __forceinline__ void batch_sums(const SampleJob &job, const uint4 *rt, const uint4 *rd, int c0,
+                                           float *wp, int tid) {
+  using E = Elt<DT>;
+  constexpr int EPV = E::kEPV;
+#pragma unroll
+  for (int u = 0; u < kFinBatch; ++u) {
+    float xt[EPV], xd[EPV];
+    E::vec(rt[u], xt);
+    E::vec(rd[u], xd);
+    float t = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) t += weight_of(job, xt[e], xd[e]);
+    t = wave_sum(t);
+    if ((tid & (kWave - 1)) == 0) wp[(c0 + u) * kFinWaves + tid / kWave] = t;
+  }
+}
+
+// Streams the job's row(s) once; wp[c * kFinWaves + wave] = wave sum of chunk c.
+// Aligned rows: chunks whose vectors are all complete go in batches of
+// kFinBatch, the next batch's loads in flight while the current one is
+// reduced; the remaining chunks (the row's end) are guarded per element.
+template <int DT, bool kVec>
+__device__ __forceinline__ void stream_chunk_sums(const SampleJob &job, int V, int C, float *wp, int tid) {
+  int c = 0;
+  if (kVec) {
+    constexpr int EPV = Elt<DT>::kEPV;
+    const int full = (V / EPV) / kFinThreads;  // chunks made of complete vectors only
+    const bool resid = job.mode == JOB_RESIDUAL;
+    const uint4 *tv = reinterpret_cast<const uint4 *>(job.t_row) + tid;
+    const uint4 *dv = reinterpret_cast<const uint4 *>(job.d_row) + tid;
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    if (full >= kFinBatch) {
+      uint4 at[kFinBatch], ad[kFinBatch], bt[kFinBatch], bd[kFinBatch];
+#pragma unroll
+      for (int u = 0; u < kFinBatch; ++u) {
+        at[u] = load_stream(tv + u * kFinThreads);
+        ad[u] = resid ? load_stream(dv + u * kFinThreads) : zero;
+      }
+      for (; c + 2 * kFinBatch <= full; c += kFinBatch) {
+#pragma unroll
+        for (int u = 0; u < kFinBatch; ++u) {
+          bt[u] = load_stream(tv + (c + kFinBatch + u) * kFinThreads);
+          bd[u] = resid ? load_stream(dv + (c + kFinBatch + u) * kFinThreads) : zero;
+        }
+        batch_sums<DT>(job, at, ad, c, wp, tid);
+#pragma unroll
+        for (int u = 0; u < kFinBatch; ++u) {
+          at[u] = bt[u];
+          ad[u] = bd[u];
+        }
+      }
+      batch_sums<DT>(job, at, ad, c, wp, tid);
+      c += kFinBatch;
+    }
+  }
+  for (; c < C; ++c) chunk_sum_guarded<DT, kVec>(job, V, c, wp, tid);
+}
+
+// Inverse CDF: Z = sum of chunk sums (chunk order), tau = v * Z, the chunk
+// holding tau, then the first k of that chunk whose running sum exceeds tau
+// (w_k > 0); if rounding leaves none, the chunk's last k with w_k > 0.
+template <int DT, bool kVec>
+__device__ int draw_token(const SampleJob &job, int V, float *wp, float *cs, int tid) {
+  using G = FinGeom<DT, kVec>;
+  const int C = (V + G::CH - 1) / G::CH;
+  __shared__ float s_base, s_tau;
+  __shared__ int s_chunk, s_cand, s_last;
+  __shared__ float s_wave_tot[kFinWaves];
+  stream_chunk_sums<DT, kVec>(job, V, C, wp, tid);
+  __syncthreads();
+  for (int c = tid; c < C; c += kFinThreads) {
+    float t = wp[c * kFinWaves];
+#pragma unroll
+    for (int w = 1; w < kFinWaves; ++w) t += wp[c * kFinWaves + w];
+    cs[c] = t;
+  }
   __syncthreads();
   if (tid == 0) {
-    float s = lds[0];
-#pragma unroll
-    for (int k = 1; k < kSampleThreads / kWave; ++k) s += lds[k];
-    spart[static_cast<int64_t>(b) * C + c] = s;
-  }
-}
-
-template <int DT>
-__global__ void __launch_bounds__(kSampleThreads) k_sample_select(const SampleJob *__restrict__ jobs,
-                                                                  int V, int C, const float *__restrict__ spart) {
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  const SampleJob job = jobs[b];
-  if (job.mode == JOB_NONE) return;
-  __shared__ float s_base, s_tau;
-  __shared__ int s_chunk;
-  __shared__ float s_wsum[kSampleThreads / kWave];
-  __shared__ int s_cand, s_last;
-  if (tid == 0) {
-    const float *sp = spart + static_cast<int64_t>(b) * C;
     float Z = 0.0f;
-    for (int c = 0; c < C; ++c) Z += sp[c];
+    for (int c = 0; c < C; ++c) Z += cs[c];
     const float tau = job.v * Z;
     int chunk = -1;
     float run = 0.0f, base = 0.0f;
     for (int c = 0; c < C; ++c) {
-      const float nxt = run + sp[c];
+      const float nxt = run + cs[c];
       if (nxt > tau) {
         chunk = c;
         base = run;
@@ -482,11 +621,11 @@ __global__ void __launch_bounds__(kSampleThreads) k_sample_select(const SampleJo
     if (chunk < 0) {  // rounding left tau at or past the total: last chunk with mass
       run = 0.0f;
       for (int c = 0; c < C; ++c) {
-        if (sp[c] > 0.0f) {
+        if (cs[c] > 0.0f) {
           chunk = c;
           base = run;
         }
-        run += sp[c];
+        run += cs[c];
       }
       if (chunk < 0) chunk = 0;
     }
@@ -497,18 +636,13 @@ __global__ void __launch_bounds__(kSampleThreads) k_sample_select(const SampleJo
     s_last = -1;
   }
   __syncthreads();
-  const int lo = s_chunk * kSampleChunk;
-  const int hi = min(V, lo + kSampleChunk);
-  const int k0 = lo + tid * kSamplePerThread;
-  float w[kSamplePerThread];
+  const int chunk = s_chunk;
+  float w[G::E];
+  thread_weights<DT, kVec>(job, V, chunk, tid, w);
   float ts = 0.0f;
 #pragma unroll
-  for (int e = 0; e < kSamplePerThread; ++e) {
-    w[e] = (k0 + e < hi) ? sample_weight<DT>(job, k0 + e) : 0.0f;
-    ts += w[e];
-  }
-  // exclusive prefix of the per-thread sums, in thread order
-  const int lane = tid & (kWave - 1);
+  for (int e = 0; e < G::E; ++e) ts += w[e];
+  const int wave = tid / kWave, lane = tid & (kWave - 1);
   float incl = ts;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
@@ -517,29 +651,49 @@ __global__ void __launch_bounds__(kSampleThreads) k_sample_select(const SampleJo
   }
   float excl = __shfl_up(incl, 1);
   if (lane == 0) excl = 0.0f;
-  if (lane == kWave - 1) s_wsum[tid / kWave] = incl;
+  if (lane == kWave - 1) s_wave_tot[wave] = incl;
   __syncthreads();
   float wave_off = 0.0f;
-  for (int k = 0; k < tid / kWave; ++k) wave_off += s_wsum[k];
+  for (int k = 0; k < wave; ++k) wave_off += s_wave_tot[k];
   float run = s_base + (wave_off + excl);
   const float tau = s_tau;
+  const int k0 = chunk * G::CH + tid * G::E;
   int cand = INT_MAX, last = -1;
 #pragma unroll
-  for (int e = 0; e < kSamplePerThread; ++e) {
-    if (k0 + e < hi) {
-      run += w[e];
-      if (cand == INT_MAX && run > tau && w[e] > 0.0f) cand = k0 + e;
-      if (w[e] > 0.0f) last = k0 + e;
-    }
+  for (int e = 0; e < G::E; ++e) {
+    run += w[e];
+    if (cand == INT_MAX && run > tau && w[e] > 0.0f) cand = k0 + e;
+    if (w[e] > 0.0f) last = k0 + e;
   }
   if (cand != INT_MAX) atomicMin(&s_cand, cand);
   if (last >= 0) atomicMax(&s_last, last);
   __syncthreads();
-  if (tid == 0) {
-    int y = s_cand != INT_MAX ? s_cand : s_last;
-    if (y < 0) y = lo;  // no mass anywhere: only reachable with invalid logits
-    *job.out_slot = y;
+  int y = s_cand != INT_MAX ? s_cand : s_last;
+  if (y < 0) y = chunk * G::CH;  // no mass anywhere: only reachable with invalid logits
+  return y;
+}
+
+// kWindow: wave 0 decides the window (job in LDS) and writes its outputs;
+// otherwise the job comes from the tree decide kernel.  Then the workgroup
+// draws the corrected / bonus token.
+template <int DT, bool kWindow>
+__global__ void __launch_bounds__(kFinThreads) k_finish(WindowArgs A, const SampleJob *__restrict__ jobs, int V) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ SampleJob s_job;
+  __shared__ float s_wp[kFinMaxChunks * kFinWaves];
+  __shared__ float s_cs[kFinMaxChunks];
+  if (kWindow) {
+    if (tid < kWave) window_decide<DT>(A, b, tid, true, &s_job);
+  } else if (tid == 0) {
+    s_job = jobs[b];
   }
+  __syncthreads();
+  const SampleJob job = s_job;
+  if (job.mode == JOB_NONE) return;
+  const int y = job_rows_aligned(job) ? draw_token<DT, true>(job, V, s_wp, s_cs, tid)
+                                      : draw_token<DT, false>(job, V, s_wp, s_cs, tid);
+  if (tid == 0) *job.out_slot = y;
 }
 
 // ---------------------------------------------------------------------------
@@ -623,11 +777,12 @@ void launch_row_stats(int dtype, bool argmax, const RowSet &rs, int64_t blocks, 
   else launch_row_stats_t<false>(dtype, rs, blocks, part, st);
 }
 
-void launch_window_decide(int dtype, const WindowArgs &A, int B, hipStream_t st) {
+void launch_window_finish(int dtype, const WindowArgs &A, int B, hipStream_t st) {
+  const dim3 grid(B), blk(kFinThreads);
   switch (dtype) {
-    case DT_BF16: hipLaunchKernelGGL(k_window_decide<DT_BF16>, dim3(B), dim3(kWave), 0, st, A); break;
-    case DT_F16: hipLaunchKernelGGL(k_window_decide<DT_F16>, dim3(B), dim3(kWave), 0, st, A); break;
-    default: hipLaunchKernelGGL(k_window_decide<DT_F32>, dim3(B), dim3(kWave), 0, st, A); break;
+    case DT_BF16: hipLaunchKernelGGL((k_finish<DT_BF16, true>), grid, blk, 0, st, A, nullptr, A.V); break;
+    case DT_F16: hipLaunchKernelGGL((k_finish<DT_F16, true>), grid, blk, 0, st, A, nullptr, A.V); break;
+    default: hipLaunchKernelGGL((k_finish<DT_F32, true>), grid, blk, 0, st, A, nullptr, A.V); break;
   }
 }
 
@@ -643,21 +798,13 @@ void launch_tree_decide(int dtype, const TreeArgs &A, int B, hipStream_t st) {
   }
 }
 
-void launch_sample(int dtype, const SampleJob *jobs, int B, int V, int C, float *spart, hipStream_t st) {
-  const dim3 g1(C, B), g2(B), blk(kSampleThreads);
+void launch_tree_finish(int dtype, const SampleJob *jobs, int B, int V, hipStream_t st) {
+  const dim3 grid(B), blk(kFinThreads);
+  const WindowArgs none{};
   switch (dtype) {
-    case DT_BF16:
-      hipLaunchKernelGGL(k_sample_partial<DT_BF16>, g1, blk, 0, st, jobs, V, C, spart);
-      hipLaunchKernelGGL(k_sample_select<DT_BF16>, g2, blk, 0, st, jobs, V, C, spart);
-      break;
-    case DT_F16:
-      hipLaunchKernelGGL(k_sample_partial<DT_F16>, g1, blk, 0, st, jobs, V, C, spart);
-      hipLaunchKernelGGL(k_sample_select<DT_F16>, g2, blk, 0, st, jobs, V, C, spart);
-      break;
-    default:
-      hipLaunchKernelGGL(k_sample_partial<DT_F32>, g1, blk, 0, st, jobs, V, C, spart);
-      hipLaunchKernelGGL(k_sample_select<DT_F32>, g2, blk, 0, st, jobs, V, C, spart);
-      break;
+    case DT_BF16: hipLaunchKernelGGL((k_finish<DT_BF16, false>), grid, blk, 0, st, none, jobs, V); break;
+    case DT_F16: hipLaunchKernelGGL((k_finish<DT_F16, false>), grid, blk, 0, st, none, jobs, V); break;
+    default: hipLaunchKernelGGL((k_finish<DT_F32, false>), grid, blk, 0, st, none, jobs, V); break;
   }
 }
 

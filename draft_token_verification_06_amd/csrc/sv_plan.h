@@ -7,28 +7,30 @@
 namespace sv {
 
 constexpr int kRowThreads = 256;      // row-statistics workgroup
-constexpr int kSampleThreads = 256;   // sampling workgroups
-constexpr int kSampleChunk = 4096;    // vocabulary elements per sampling chunk
-constexpr int kSamplePerThread = kSampleChunk / kSampleThreads;
+constexpr int kFinThreads = 1024;     // sampling workgroup (one per sequence)
+constexpr int kFinWaves = kFinThreads / 64;
+constexpr int kFinBatch = 2;          // chunks per pipelined batch
+constexpr int kMaxVocab = 1 << 21;    // 2,097,152 tokens
+constexpr int kFinMaxChunks = kMaxVocab / (kFinThreads * 4);  // 512
 constexpr int kMaxSegments = 64;      // row segments (split-row mode)
-constexpr int64_t kFillWorkgroups = 2048;  // enough workgroups for 256 CUs
+constexpr int64_t kFillWorkgroups = 16384;  // row workgroups per launch (256 CUs)
 constexpr int kMinSegment = 4096;     // elements; below this a split does not pay
 
 // Work item of the sampling pass of one sequence: draw from
 //   w_k = p_k                       (BONUS)
 //   w_k = max(0, p_k - q_k)         (RESIDUAL)
-// with p_k = 2^(t_k log2e - mt_l2e) * inv_st, q_k likewise from the draft row.
+// with p_k = 2^(t_k log2e - ct), q_k = 2^(d_k log2e - cd); the offsets carry
+// the row maximum and the log of the row's normaliser.
 enum : int { JOB_NONE = 0, JOB_BONUS = 1, JOB_RESIDUAL = 2 };
 
 struct SampleJob {
   const void *t_row;
   const void *d_row;
   int32_t *out_slot;  // where the drawn token is stored
-  float mt_l2e, inv_st;
-  float md_l2e, inv_sd;
+  float ct, cd;
   float v;            // sampling uniform
   int32_t mode;
-  int32_t pad[4];
+  int32_t pad[6];
 };
 static_assert(sizeof(SampleJob) == 64, "SampleJob is one 64-byte record");
 
@@ -62,16 +64,13 @@ inline RowPlan plan_rows(int64_t rows_total, int32_t V) {
   return {static_cast<int>(S), static_cast<int>(seg)};
 }
 
-inline int sample_chunks(int32_t V) { return (V + kSampleChunk - 1) / kSampleChunk; }
-
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace sections (byte offsets); rows_per_seq counts target + draft rows.
 struct Layout {
   RowPlan plan;
   int rows_per_seq;
-  int chunks;
-  size_t part_off, jobs_off, spart_off, total;
+  size_t part_off, jobs_off, total;
 };
 
 // op: 0 window, 1 greedy, 2 tree (n = gamma or N).
@@ -81,14 +80,11 @@ inline Layout make_layout(int op, int64_t B, int32_t n, int32_t V) {
   else if (op == 1) L.rows_per_seq = n + 1;
   else L.rows_per_seq = 2 * n;
   L.plan = plan_rows(B * L.rows_per_seq, V);
-  L.chunks = (op == 1) ? 0 : sample_chunks(V);
   size_t off = 0;
   L.part_off = off;
   off = align256(off + sizeof(float) * 2 * static_cast<size_t>(B) * L.rows_per_seq * L.plan.S);
   L.jobs_off = off;
   off = align256(off + (op == 1 ? 0 : sizeof(SampleJob) * static_cast<size_t>(B)));
-  L.spart_off = off;
-  off = align256(off + sizeof(float) * static_cast<size_t>(B) * L.chunks);
   L.total = off;
   return L;
 }

@@ -112,6 +112,26 @@ int sv_verify_window(const void *target_logits, int64_t target_seq_stride,
                      float *p_draft, float *q_draft,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* sv_verify_window in two halves on the same workspace and arguments:
+ *   part SV_PART_ROW_STATS     -- the streaming pass over every needed logits
+ *                                 row (the call's HBM traffic);
+ *   part SV_PART_DECIDE_SAMPLE -- accept decisions, first rejection and the
+ *                                 residual / bonus draw.
+ * Running ROW_STATS then DECIDE_SAMPLE on one stream equals one
+ * sv_verify_window call bit for bit.  Lets a caller overlap the streaming pass
+ * with other work or time it on its own. */
+#define SV_PART_ROW_STATS 1
+#define SV_PART_DECIDE_SAMPLE 2
+int sv_verify_window_part(int part, const void *target_logits, int64_t target_seq_stride,
+                          const void *draft_logits, int64_t draft_seq_stride, int dtype,
+                          const int32_t *draft_tokens, const int32_t *window_len,
+                          int32_t B, int32_t gamma, int32_t V,
+                          uint64_t seed, uint64_t tag, const uint64_t *seq_ids,
+                          const int64_t *base_pos,
+                          int32_t *n_accepted, int32_t *out_tokens,
+                          float *p_draft, float *q_draft,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Greedy window verification (temperature 0).  Same layouts as
  * sv_verify_window; only target rows 0..window_len are read.  n is the first
  * i < len with draft_tokens[i] != argmax(row i) (smallest index among equal

@@ -126,7 +126,7 @@ def run_hierarchy_and_check(h, g1, g2, cap, mode, rows):
         r1 = sv.verify_greedy(S1, o0)
     else:
         r1 = sv.verify_window(S1, S0, o0, seed=0, tag=1)
-    bt[:, 1, : g1 + 1] = r1.out_tokens
+    bt[:, 1, : g1 + 1] = r1.out_tokens.clamp(min=0)  # slots past the length hold 0
     bl[:, 1] = r1.n_accepted + 1
     sv.rollback(bt, bl, 1, r1.out_tokens, r1.n_accepted, len_offset=1)
     wl2 = torch.clamp(r1.n_accepted + 1, max=g2).to(torch.int32)
@@ -135,7 +135,7 @@ def run_hierarchy_and_check(h, g1, g2, cap, mode, rows):
         r2 = sv.verify_greedy(F[:, : g2 + 1], toks2, window_len=wl2)
     else:
         r2 = sv.verify_window(F[:, : g2 + 1], S1[:, :g2], toks2, seed=0, tag=2, window_len=wl2)
-    bt[:, 2, : g2 + 1] = r2.out_tokens
+    bt[:, 2, : g2 + 1] = r2.out_tokens.clamp(min=0)
     bl[:, 2] = r2.n_accepted + 1
     sv.rollback(bt, bl, 2, r2.out_tokens, r2.n_accepted, len_offset=1)
     torch.cuda.synchronize()
