@@ -19,6 +19,7 @@ timed on this host.  Smaller workloads (greedy, tree, hierarchy, latency
 configs) are timed in the same run and reported under "also".
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +29,24 @@ B, GAMMA, V = 256, 8, 128256
 ALPHAS = (0.05, 0.3, 0.6, 0.9)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "verified draft tokens/s + achieved HBM GB/s, γ=8 window, vocab 128256 bf16"
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("sv_kernels.hip", "sv_device.h", "sv_plan.h")
+
+# HBM bytes per launch of the row-statistics kernel on this workload, from
+# `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` runs of this script
+# (commands and raw figures in profiles/k_row_stats_window_b256_g8_v128256_bf16.md),
+# each scaled by the same counter on the 1 GiB copy this script performs
+# (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000).  Valid for the kernel sources whose
+# hash is recorded; reported as null for any other build.
+PMC_TRAFFIC = {"kernel_sha": "ff009fa8b340ccdb", "bytes": 1117001060}
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(HERE, "draft_token_verification_06_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -153,7 +172,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": rs_gbps / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": PMC_TRAFFIC["bytes"] if PMC_TRAFFIC["kernel_sha"] == kernel_sha() else None,
+            "kernel_sha": kernel_sha(),
             "avg_launch_us": rs_ms * 1e3,
             "bytes_per_launch": alg_bytes,
             "frac_of_probe_read": rs_gbps / probe_gbps,

@@ -357,7 +357,8 @@ int sv_rollback(int32_t *buf_tokens, int32_t *buf_len, int32_t S, int32_t K,
 int32_t sv_probe_blocks(size_t bytes) { return probe_blocks(bytes); }
 
 int sv_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream) {
-  if (!src || !sink || bytes < 16 || bytes % 16 != 0 || !aligned(src, 16)) return SV_EINVAL;
+  if (!src || !sink || bytes < 16 || bytes % 16 != 0 || bytes > (size_t(1) << 40) || !aligned(src, 16))
+    return SV_EINVAL;
   launch_probe_read(src, bytes, sink, stream);
   return launch_status();
 }

@@ -729,22 +729,28 @@ __global__ void __launch_bounds__(kWave) k_rollback(RollbackArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-// Read-bandwidth probe
+// Read-bandwidth probe: each workgroup streams one contiguous chunk with the
+// same nontemporal 16-byte loads as the row pass, kUnroll loads per thread in
+// flight, and folds the words into a checksum.
 // ---------------------------------------------------------------------------
+constexpr int64_t kProbeChunk = 16384;  // 16-byte vectors per workgroup (256 KiB)
+
 __global__ void __launch_bounds__(kRowThreads) k_probe_read(const uint4 *__restrict__ src, int64_t nvec,
                                                             uint32_t *__restrict__ sink) {
+  const int64_t lo = static_cast<int64_t>(blockIdx.x) * kProbeChunk;
+  const int64_t n = min(kProbeChunk, nvec - lo);
+  const uint4 *p = src + lo;
   uint32_t acc = 0;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kRowThreads;
-  int64_t i = static_cast<int64_t>(blockIdx.x) * kRowThreads + threadIdx.x;
-  for (; i + (kUnroll - 1) * stride < nvec; i += kUnroll * stride) {
+  int64_t v0 = 0;
+  for (; v0 + kUnroll * kRowThreads <= n; v0 += kUnroll * kRowThreads) {
     uint4 r[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) r[u] = src[i + u * stride];
+    for (int u = 0; u < kUnroll; ++u) r[u] = load_stream(p + v0 + u * kRowThreads + threadIdx.x);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
   }
-  for (; i < nvec; i += stride) {
-    const uint4 r = src[i];
+  for (int64_t i = v0 + threadIdx.x; i < n; i += kRowThreads) {
+    const uint4 r = load_stream(p + i);
     acc ^= r.x ^ r.y ^ r.z ^ r.w;
   }
 #pragma unroll
@@ -814,10 +820,7 @@ void launch_rollback(const RollbackArgs &A, int S, int stage, hipStream_t st) {
 
 int probe_blocks(size_t bytes) {
   const int64_t nvec = static_cast<int64_t>(bytes / 16);
-  int64_t blocks = (nvec + kRowThreads - 1) / kRowThreads;
-  if (blocks > 4096) blocks = 4096;
-  if (blocks < 1) blocks = 1;
-  return static_cast<int>(blocks);
+  return static_cast<int>((nvec + kProbeChunk - 1) / kProbeChunk);
 }
 
 void launch_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t st) {

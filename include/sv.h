@@ -194,10 +194,11 @@ int sv_rollback(int32_t *buf_tokens, int32_t *buf_len, int32_t S, int32_t K,
                 const int32_t *verified_len, int32_t len_offset,
                 hipStream_t stream);
 
-/* Diagnostic: stream `bytes` (a multiple of 16, 16-byte aligned) of device
- * memory through the same 16-byte vector loads the verification kernels use
- * and write one 32-bit checksum per workgroup to `sink` [sv_probe_blocks()];
- * measures the read bandwidth ceiling on the running GPU. */
+/* Diagnostic: stream `bytes` (a multiple of 16, 16-byte aligned, at most
+ * 2^40) of device memory through the same nontemporal 16-byte loads the row
+ * pass uses, one contiguous 256 KiB chunk per workgroup, and write one 32-bit
+ * checksum per workgroup to `sink` [sv_probe_blocks(bytes)]; measures the read
+ * bandwidth ceiling of the running GPU. */
 int32_t sv_probe_blocks(size_t bytes);
 int sv_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
 
