@@ -166,7 +166,7 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
   A.p_draft = p_draft;
   A.q_draft = q_draft;
   A.jobs = jobs;
-  launch_window_finish(dtype, A, B, stream);
+  launch_window_finish(dtype, A, B, reinterpret_cast<float *>(wsb + L.spart_off), L.cmax, stream);
   return launch_status();
 }
 
@@ -328,7 +328,8 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
   A.jobs = jobs;
   A.meta = meta;
   launch_tree_decide(dtype, A, B, stream);
-  if (mode == SV_TREE_STOCHASTIC) launch_tree_finish(dtype, jobs, B, V, stream);
+  if (mode == SV_TREE_STOCHASTIC)
+    launch_tree_finish(dtype, jobs, B, V, reinterpret_cast<float *>(wsb + L.spart_off), L.cmax, stream);
   return launch_status();
 }
 

@@ -265,19 +265,21 @@ __device__ void window_decide(const WindowArgs &A, int b, int i, bool write, Sam
   const uint64_t seq = A.seq_ids ? A.seq_ids[b] : static_cast<uint64_t>(b);
   const int64_t base = A.base_pos ? A.base_pos[b] : 0;
 
+  // Row results of target row i (i <= gamma) and draft row i (i < gamma) are
+  // loaded whatever the window length (rows past it hold stale values and are
+  // not used), so they travel with the token loads; only the two logit
+  // gathers wait for the token.
   MaxSum st{0.0f, 1.0f}, sd{0.0f, 1.0f};
-  float P = 0.0f, Q = 0.0f, vi = 0.0f;
+  if (i <= A.gamma) st = row_maxsum(prow + i * A.S, A.S);
+  if (i < A.gamma) sd = row_maxsum(prow + (A.gamma + 1 + i) * A.S, A.S);
+  const U64x4 w = philox4x64_10({seq, static_cast<uint64_t>(base + 1 + i), 0, 0}, A.seed, A.tag);
+  const float vi = uniform24(w.c1);
+  float P = 0.0f, Q = 0.0f;
   bool acc = false;
-  if (i <= len) {  // target row i (row len is the bonus row)
-    st = row_maxsum(prow + i * A.S, A.S);
-    const U64x4 w = philox4x64_10({seq, static_cast<uint64_t>(base + 1 + i), 0, 0}, A.seed, A.tag);
-    vi = uniform24(w.c1);
-    if (i < len) {
-      sd = row_maxsum(prow + (A.gamma + 1 + i) * A.S, A.S);
-      P = prob_at(E::one(trow0 + i * row_bytes, x), st);
-      Q = prob_at(E::one(drow0 + i * row_bytes, x), sd);
-      acc = uniform24(w.c0) * Q < P;
-    }
+  if (i < len) {
+    P = prob_at(E::one(trow0 + i * row_bytes, x), st);
+    Q = prob_at(E::one(drow0 + i * row_bytes, x), sd);
+    acc = uniform24(w.c0) * Q < P;
   }
   const uint64_t inv = ~static_cast<uint64_t>(__ballot(acc));
   int n = inv ? __builtin_ctzll(inv) : kWave;
@@ -543,26 +545,28 @@ __device__ __forceinline__ void batch_sums(const SampleJob &job, const uint4 *rt
   }
 }
 
-// Streams the job's row(s) once; wp[c * kFinWaves + wave] = wave sum of chunk c.
-// Aligned rows: chunks whose vectors are all complete go in batches of
-// kFinBatch, the next batch's loads in flight while the current one is
-// reduced; the remaining chunks (the row's end) are guarded per element.
+// Streams chunks [c_begin, c_end) of the job's row(s) once;
+// wp[c * kFinWaves + wave] = wave sum of chunk c.  Aligned rows: chunks whose
+// vectors are all complete go in batches of kFinBatch, the next batch's loads
+// in flight while the current one is reduced; other chunks (the row's end) are
+// guarded per element.
 template <int DT, bool kVec>
-__device__ __forceinline__ void stream_chunk_sums(const SampleJob &job, int V, int C, float *wp, int tid) {
-  int c = 0;
+__device__ __forceinline__ void stream_chunk_sums(const SampleJob &job, int V, int c_begin, int c_end, float *wp,
+                                                  int tid) {
+  int c = c_begin;
   if (kVec) {
     constexpr int EPV = Elt<DT>::kEPV;
-    const int full = (V / EPV) / kFinThreads;  // chunks made of complete vectors only
+    const int full = min(c_end, (V / EPV) / kFinThreads);  // chunks of complete vectors only
     const bool resid = job.mode == JOB_RESIDUAL;
     const uint4 *tv = reinterpret_cast<const uint4 *>(job.t_row) + tid;
     const uint4 *dv = reinterpret_cast<const uint4 *>(job.d_row) + tid;
     const uint4 zero = make_uint4(0, 0, 0, 0);
-    if (full >= kFinBatch) {
+    if (full - c >= kFinBatch) {
       uint4 at[kFinBatch], ad[kFinBatch], bt[kFinBatch], bd[kFinBatch];
 #pragma unroll
       for (int u = 0; u < kFinBatch; ++u) {
-        at[u] = load_stream(tv + u * kFinThreads);
-        ad[u] = resid ? load_stream(dv + u * kFinThreads) : zero;
+        at[u] = load_stream(tv + (c + u) * kFinThreads);
+        ad[u] = resid ? load_stream(dv + (c + u) * kFinThreads) : zero;
       }
       for (; c + 2 * kFinBatch <= full; c += kFinBatch) {
 #pragma unroll
@@ -581,28 +585,29 @@ __device__ __forceinline__ void stream_chunk_sums(const SampleJob &job, int V, i
       c += kFinBatch;
     }
   }
-  for (; c < C; ++c) chunk_sum_guarded<DT, kVec>(job, V, c, wp, tid);
+  for (; c < c_end; ++c) chunk_sum_guarded<DT, kVec>(job, V, c, wp, tid);
 }
 
-// Inverse CDF: Z = sum of chunk sums (chunk order), tau = v * Z, the chunk
-// holding tau, then the first k of that chunk whose running sum exceeds tau
-// (w_k > 0); if rounding leaves none, the chunk's last k with w_k > 0.
-template <int DT, bool kVec>
-__device__ int draw_token(const SampleJob &job, int V, float *wp, float *cs, int tid) {
-  using G = FinGeom<DT, kVec>;
-  const int C = (V + G::CH - 1) / G::CH;
-  __shared__ float s_base, s_tau;
-  __shared__ int s_chunk, s_cand, s_last;
-  __shared__ float s_wave_tot[kFinWaves];
-  stream_chunk_sums<DT, kVec>(job, V, C, wp, tid);
-  __syncthreads();
-  for (int c = tid; c < C; c += kFinThreads) {
+// cs[c] = sum over waves of wp[c][wave], in wave order, for c in [c_begin, c_end).
+__device__ __forceinline__ void chunk_totals(const float *wp, int c_begin, int c_end, float *cs, int tid) {
+  for (int c = c_begin + tid; c < c_end; c += kFinThreads) {
     float t = wp[c * kFinWaves];
 #pragma unroll
     for (int w = 1; w < kFinWaves; ++w) t += wp[c * kFinWaves + w];
     cs[c] = t;
   }
-  __syncthreads();
+}
+
+// Inverse CDF from the chunk sums cs[0..C): Z = their sum in chunk order,
+// tau = v * Z, the chunk holding tau, then the first k of that chunk whose
+// running sum exceeds tau (w_k > 0); if rounding leaves none, the chunk's last
+// k with w_k > 0.  cs must be visible to the whole workgroup.
+template <int DT, bool kVec>
+__device__ int draw_from_sums(const SampleJob &job, int V, int C, const float *cs, int tid) {
+  using G = FinGeom<DT, kVec>;
+  __shared__ float s_base, s_tau;
+  __shared__ int s_chunk, s_cand, s_last;
+  __shared__ float s_wave_tot[kFinWaves];
   if (tid == 0) {
     float Z = 0.0f;
     for (int c = 0; c < C; ++c) Z += cs[c];
@@ -673,9 +678,26 @@ __device__ int draw_token(const SampleJob &job, int V, float *wp, float *cs, int
   return y;
 }
 
-// kWindow: wave 0 decides the window (job in LDS) and writes its outputs;
-// otherwise the job comes from the tree decide kernel.  Then the workgroup
-// draws the corrected / bonus token.
+template <int DT, bool kVec>
+__device__ __forceinline__ int finish_chunks(int V) {
+  return (V + FinGeom<DT, kVec>::CH - 1) / FinGeom<DT, kVec>::CH;
+}
+
+// Job of sequence b into s_job: decided here (window, wave 0; writes the
+// window outputs when `write`) or read from the tree decide kernel.
+template <int DT, bool kWindow>
+__device__ __forceinline__ void load_job(const WindowArgs &A, const SampleJob *jobs, int b, bool write,
+                                         SampleJob *s_job, int tid) {
+  if (kWindow) {
+    if (tid < kWave) window_decide<DT>(A, b, tid, write, s_job);
+  } else if (tid == 0) {
+    *s_job = jobs[b];
+  }
+  __syncthreads();
+}
+
+// One workgroup per sequence (large batches): decide, one pass over the
+// row(s) with chunk sums in LDS, draw.
 template <int DT, bool kWindow>
 __global__ void __launch_bounds__(kFinThreads) k_finish(WindowArgs A, const SampleJob *__restrict__ jobs, int V) {
   const int b = blockIdx.x;
@@ -683,16 +705,71 @@ __global__ void __launch_bounds__(kFinThreads) k_finish(WindowArgs A, const Samp
   __shared__ SampleJob s_job;
   __shared__ float s_wp[kFinMaxChunks * kFinWaves];
   __shared__ float s_cs[kFinMaxChunks];
-  if (kWindow) {
-    if (tid < kWave) window_decide<DT>(A, b, tid, true, &s_job);
-  } else if (tid == 0) {
-    s_job = jobs[b];
-  }
-  __syncthreads();
+  load_job<DT, kWindow>(A, jobs, b, true, &s_job, tid);
   const SampleJob job = s_job;
   if (job.mode == JOB_NONE) return;
-  const int y = job_rows_aligned(job) ? draw_token<DT, true>(job, V, s_wp, s_cs, tid)
-                                      : draw_token<DT, false>(job, V, s_wp, s_cs, tid);
+  int y;
+  if (job_rows_aligned(job)) {
+    const int C = finish_chunks<DT, true>(V);
+    stream_chunk_sums<DT, true>(job, V, 0, C, s_wp, tid);
+    __syncthreads();
+    chunk_totals(s_wp, 0, C, s_cs, tid);
+    __syncthreads();
+    y = draw_from_sums<DT, true>(job, V, C, s_cs, tid);
+  } else {
+    const int C = finish_chunks<DT, false>(V);
+    stream_chunk_sums<DT, false>(job, V, 0, C, s_wp, tid);
+    __syncthreads();
+    chunk_totals(s_wp, 0, C, s_cs, tid);
+    __syncthreads();
+    y = draw_from_sums<DT, false>(job, V, C, s_cs, tid);
+  }
+  if (tid == 0) *job.out_slot = y;
+}
+
+// Small batches, part 1, grid (B, G): workgroup g decides (redundantly, it is
+// cheap) and sums its share of the chunks into spart[b][c]; the g = 0
+// workgroup writes the window outputs and the job.
+template <int DT, bool kWindow>
+__global__ void __launch_bounds__(kFinThreads) k_finish_part(WindowArgs A, SampleJob *__restrict__ jobs, int V,
+                                                            float *__restrict__ spart, int cmax) {
+  const int b = blockIdx.x;
+  const int g = blockIdx.y;
+  const int G = gridDim.y;
+  const int tid = threadIdx.x;
+  __shared__ SampleJob s_job;
+  __shared__ float s_wp[kFinMaxChunks * kFinWaves];
+  __shared__ float s_cs[kFinMaxChunks];
+  load_job<DT, kWindow>(A, jobs, b, g == 0, &s_job, tid);
+  const SampleJob job = s_job;
+  if (kWindow && g == 0 && tid == 0) jobs[b] = job;
+  if (job.mode == JOB_NONE) return;
+  const bool vec = job_rows_aligned(job);
+  const int C = vec ? finish_chunks<DT, true>(V) : finish_chunks<DT, false>(V);
+  const int c0 = static_cast<int>(static_cast<int64_t>(C) * g / G);
+  const int c1 = static_cast<int>(static_cast<int64_t>(C) * (g + 1) / G);
+  if (vec) stream_chunk_sums<DT, true>(job, V, c0, c1, s_wp, tid);
+  else stream_chunk_sums<DT, false>(job, V, c0, c1, s_wp, tid);
+  __syncthreads();
+  chunk_totals(s_wp, c0, c1, s_cs, tid);
+  __syncthreads();
+  for (int c = c0 + tid; c < c1; c += kFinThreads) spart[static_cast<int64_t>(b) * cmax + c] = s_cs[c];
+}
+
+// Small batches, part 2, one workgroup per sequence: the draw from the chunk sums.
+template <int DT>
+__global__ void __launch_bounds__(kFinThreads) k_finish_select(const SampleJob *__restrict__ jobs, int V,
+                                                              const float *__restrict__ spart, int cmax) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ float s_cs[kFinMaxChunks];
+  const SampleJob job = jobs[b];
+  if (job.mode == JOB_NONE) return;
+  const bool vec = job_rows_aligned(job);
+  const int C = vec ? finish_chunks<DT, true>(V) : finish_chunks<DT, false>(V);
+  for (int c = tid; c < C; c += kFinThreads) s_cs[c] = spart[static_cast<int64_t>(b) * cmax + c];
+  __syncthreads();
+  const int y = vec ? draw_from_sums<DT, true>(job, V, C, s_cs, tid) : draw_from_sums<DT, false>(job, V, C, s_cs, tid);
   if (tid == 0) *job.out_slot = y;
 }
 
@@ -783,13 +860,40 @@ void launch_row_stats(int dtype, bool argmax, const RowSet &rs, int64_t blocks, 
   else launch_row_stats_t<false>(dtype, rs, blocks, part, st);
 }
 
-void launch_window_finish(int dtype, const WindowArgs &A, int B, hipStream_t st) {
-  const dim3 grid(B), blk(kFinThreads);
-  switch (dtype) {
-    case DT_BF16: hipLaunchKernelGGL((k_finish<DT_BF16, true>), grid, blk, 0, st, A, nullptr, A.V); break;
-    case DT_F16: hipLaunchKernelGGL((k_finish<DT_F16, true>), grid, blk, 0, st, A, nullptr, A.V); break;
-    default: hipLaunchKernelGGL((k_finish<DT_F32, true>), grid, blk, 0, st, A, nullptr, A.V); break;
+// Workgroups per sequence for the draw: enough to give every CU work, at
+// most one per chunk of the vector geometry.
+static int finish_split(int B, int V, int dtype) {
+  const int epv = dtype == DT_F32 ? 4 : 8;
+  const int chunks = (V + kFinThreads * epv - 1) / (kFinThreads * epv);
+  int G = (kFinFillWorkgroups + B - 1) / B;
+  if (G > chunks) G = chunks;
+  return G < 1 ? 1 : G;
+}
+
+template <int DT, bool kWindow>
+static void launch_finish_t(const WindowArgs &A, SampleJob *jobs, int B, int V, float *spart, int cmax,
+                            hipStream_t st) {
+  const int G = finish_split(B, V, DT);
+  if (G == 1) {
+    hipLaunchKernelGGL((k_finish<DT, kWindow>), dim3(B), dim3(kFinThreads), 0, st, A, jobs, V);
+  } else {
+    hipLaunchKernelGGL((k_finish_part<DT, kWindow>), dim3(B, G), dim3(kFinThreads), 0, st, A, jobs, V, spart, cmax);
+    hipLaunchKernelGGL(k_finish_select<DT>, dim3(B), dim3(kFinThreads), 0, st, jobs, V, spart, cmax);
   }
+}
+
+template <bool kWindow>
+static void launch_finish(int dtype, const WindowArgs &A, SampleJob *jobs, int B, int V, float *spart, int cmax,
+                          hipStream_t st) {
+  switch (dtype) {
+    case DT_BF16: launch_finish_t<DT_BF16, kWindow>(A, jobs, B, V, spart, cmax, st); break;
+    case DT_F16: launch_finish_t<DT_F16, kWindow>(A, jobs, B, V, spart, cmax, st); break;
+    default: launch_finish_t<DT_F32, kWindow>(A, jobs, B, V, spart, cmax, st); break;
+  }
+}
+
+void launch_window_finish(int dtype, const WindowArgs &A, int B, float *spart, int cmax, hipStream_t st) {
+  launch_finish<true>(dtype, A, A.jobs, B, A.V, spart, cmax, st);
 }
 
 void launch_greedy_decide(const GreedyArgs &A, int B, hipStream_t st) {
@@ -804,14 +908,9 @@ void launch_tree_decide(int dtype, const TreeArgs &A, int B, hipStream_t st) {
   }
 }
 
-void launch_tree_finish(int dtype, const SampleJob *jobs, int B, int V, hipStream_t st) {
-  const dim3 grid(B), blk(kFinThreads);
+void launch_tree_finish(int dtype, SampleJob *jobs, int B, int V, float *spart, int cmax, hipStream_t st) {
   const WindowArgs none{};
-  switch (dtype) {
-    case DT_BF16: hipLaunchKernelGGL((k_finish<DT_BF16, false>), grid, blk, 0, st, none, jobs, V); break;
-    case DT_F16: hipLaunchKernelGGL((k_finish<DT_F16, false>), grid, blk, 0, st, none, jobs, V); break;
-    default: hipLaunchKernelGGL((k_finish<DT_F32, false>), grid, blk, 0, st, none, jobs, V); break;
-  }
+  launch_finish<false>(dtype, none, jobs, B, V, spart, cmax, st);
 }
 
 void launch_rollback(const RollbackArgs &A, int S, int stage, hipStream_t st) {

@@ -7,11 +7,18 @@
 namespace sv {
 
 constexpr int kRowThreads = 256;      // row-statistics workgroup
-constexpr int kFinThreads = 1024;     // sampling workgroup (one per sequence)
+#ifndef SV_FIN_THREADS
+#define SV_FIN_THREADS 1024
+#endif
+#ifndef SV_FIN_BATCH
+#define SV_FIN_BATCH 2
+#endif
+constexpr int kFinThreads = SV_FIN_THREADS;  // sampling workgroup (one per sequence)
 constexpr int kFinWaves = kFinThreads / 64;
-constexpr int kFinBatch = 2;          // chunks per pipelined batch
+constexpr int kFinBatch = SV_FIN_BATCH;      // chunks per pipelined batch
 constexpr int kMaxVocab = 1 << 21;    // 2,097,152 tokens
-constexpr int kFinMaxChunks = kMaxVocab / (kFinThreads * 4);  // 512
+constexpr int kFinMaxChunks = kMaxVocab / (kFinThreads * 4);  // 512 at 1024 threads
+constexpr int kFinFillWorkgroups = 256;  // draw workgroups wanted per launch
 constexpr int kMaxSegments = 64;      // row segments (split-row mode)
 constexpr int64_t kFillWorkgroups = 16384;  // row workgroups per launch (256 CUs)
 constexpr int kMinSegment = 4096;     // elements; below this a split does not pay
@@ -70,7 +77,8 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct Layout {
   RowPlan plan;
   int rows_per_seq;
-  size_t part_off, jobs_off, total;
+  int cmax;  // chunk sums per sequence in the split draw
+  size_t part_off, jobs_off, spart_off, total;
 };
 
 // op: 0 window, 1 greedy, 2 tree (n = gamma or N).
@@ -85,6 +93,9 @@ inline Layout make_layout(int op, int64_t B, int32_t n, int32_t V) {
   off = align256(off + sizeof(float) * 2 * static_cast<size_t>(B) * L.rows_per_seq * L.plan.S);
   L.jobs_off = off;
   off = align256(off + (op == 1 ? 0 : sizeof(SampleJob) * static_cast<size_t>(B)));
+  L.cmax = (op == 1) ? 0 : (V + kFinThreads * 4 - 1) / (kFinThreads * 4);
+  L.spart_off = off;
+  off = align256(off + sizeof(float) * static_cast<size_t>(B) * L.cmax);
   L.total = off;
   return L;
 }
