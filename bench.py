@@ -130,6 +130,30 @@ def main():
     rs_gbps = alg_bytes / (rs_ms * 1e-3) / 1e9
     step_gbps = alg_bytes / (ms_per_step * 1e-3) / 1e9
 
+    # early exit on the same batches: time per step and the row bytes it reads
+    def step_early(k):
+        a = k % len(ALPHAS)
+        d = data[a]
+        sv.verify_window(d["target"], d["draft"], d["tokens"], seed=0, ws=ws[a], out=outs[a],
+                         early_exit=True)
+
+    for k in range(args.warmup):
+        step_early(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step_early(k)
+    torch.cuda.synchronize()
+    ee_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ee_alpha = {}
+    for a_idx, a in enumerate(ALPHAS):
+        ms = event_time_ms(torch, lambda: step_early(a_idx), 20)
+        nbytes = early_exit_rows(ref[a_idx][0], GAMMA) * V * 2
+        ee_alpha[str(a)] = {"us": ms * 1e3, "row_bytes": nbytes,
+                            "GBps_read": nbytes / (ms * 1e-3) / 1e9,
+                            "verified_drafts_per_s": B * GAMMA / (ms * 1e-3)}
+    ee_bytes = sum(v["row_bytes"] for v in ee_alpha.values()) / len(ALPHAS)
+
     # read ceiling of this GPU through the same 16-byte loads (2 GiB, beyond the MALL)
     probe_buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
     probe_buf.fill_(1)
@@ -181,6 +205,14 @@ def main():
         "breakdown_us": {"row_stats": rs_ms * 1e3, "decide_sample": ds_ms * 1e3,
                          "full_call_events": full_ms * 1e3},
         "probe_read_GBps": probe_gbps,
+        "early_exit": {
+            "entry": "sv_verify_window_early_exit (same outputs; rows after the first rejection unread)",
+            "ms_per_step": ee_ms,
+            "verified_drafts_per_s": B * GAMMA / (ee_ms * 1e-3),
+            "row_bytes_per_step_mean": ee_bytes,
+            "GBps_read": ee_bytes / (ee_ms * 1e-3) / 1e9,
+            "per_alpha": ee_alpha,
+        },
         "bytes_per_verified_draft": alg_bytes / (B * GAMMA),
         "gen_seconds": t_gen,
     }
@@ -199,6 +231,25 @@ def main():
     if not args.no_also:
         line["also"] = side_workloads(torch, sv, synth, dev)
     print(json.dumps(line), flush=True)
+
+
+def early_exit_rows(n_accepted, gamma):
+    """Rows sv_verify_window_early_exit reads for full windows: every row of
+    each position block up to the block holding the sequence's decision
+    (blocks [0,1), [1,3), [3,7), ... over target rows 0..gamma)."""
+    blocks = []
+    lo, width = 0, 1
+    while lo <= gamma:
+        hi = min(gamma + 1, lo + width)
+        blocks.append((lo, hi))
+        lo, width = hi, width * 2
+    rows = 0
+    for n in n_accepted:
+        for lo, hi in blocks:
+            rows += (hi - lo) + max(0, min(hi, gamma) - lo)
+            if n < hi:
+                break
+    return rows
 
 
 def cpu_baseline(data, ref, budget_s):

@@ -93,9 +93,10 @@ SV_PART_ROW_STATS, SV_PART_DECIDE_SAMPLE = 1, 2
 
 
 def verify_window(target, draft, tokens, *, seed=0, tag=0, window_len=None, seq_ids=None,
-                  base_pos=None, return_probs=False, ws=None, out=None, part=None):
-    """Stochastic window verification: sv_verify_window, or one half of it
-    (sv_verify_window_part) when part is SV_PART_ROW_STATS / SV_PART_DECIDE_SAMPLE."""
+                  base_pos=None, return_probs=False, ws=None, out=None, part=None, early_exit=False):
+    """Stochastic window verification: sv_verify_window, one half of it
+    (sv_verify_window_part) when part is SV_PART_ROW_STATS / SV_PART_DECIDE_SAMPLE,
+    or sv_verify_window_early_exit when early_exit is set."""
     B, rows, V = target.shape
     gamma = rows - 1
     ts = _logits(target, gamma + 1, "target")
@@ -115,7 +116,12 @@ def verify_window(target, draft, tokens, *, seed=0, tag=0, window_len=None, seq_
         if return_probs:
             out.p_draft = torch.empty(B, gamma, dtype=torch.float32, device=dev)
             out.q_draft = torch.empty(B, gamma, dtype=torch.float32, device=dev)
-    head = (lib().sv_verify_window,) if part is None else (lib().sv_verify_window_part, part)
+    if early_exit:
+        if part is not None:
+            raise ValueError("early_exit has no parts")
+        head = (lib().sv_verify_window_early_exit,)
+    else:
+        head = (lib().sv_verify_window,) if part is None else (lib().sv_verify_window_part, part)
     with torch.cuda.device(dev):
         _check(head[0](
             *head[1:], _ptr(target), ts, _ptr(draft), ds, _DTYPE_CODE[target.dtype],

@@ -1,6 +1,7 @@
 // C-ABI entry points of libspecverify.so: argument validation, workspace
 // carving and kernel dispatch.  No allocation, no synchronisation; every
 // launch goes to the caller's stream.
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 
@@ -100,7 +101,10 @@ size_t sv_workspace_size(int op, int32_t B, int32_t n, int32_t V, int dtype) {
 
 namespace {
 
-// parts: bit 0 = row statistics, bit 1 = decide + sampling.
+constexpr int kPartRows = 1, kPartFinish = 2, kEarlyExit = 4;
+
+// parts: kPartRows = row statistics, kPartFinish = decide + draw; kEarlyExit:
+// rows in position blocks, each followed by a decide, then the draw.
 int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
                 const void *draft_logits, int64_t draft_seq_stride, int dtype,
                 const int32_t *draft_tokens, const int32_t *window_len,
@@ -136,15 +140,20 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
   rs.d_stride_bytes = draft_seq_stride * eb;
   rs.rows_t = gamma + 1;
   rs.rows_d = gamma;
+  rs.t0 = rs.d0 = 0;
+  rs.R_out = 2 * gamma + 1;
+  rs.t_slot0 = 0;
+  rs.d_slot0 = gamma + 1;
   rs.window_len = window_len;
+  rs.status = nullptr;
   rs.gamma = gamma;
   rs.V = V;
   rs.S = L.plan.S;
   rs.seg_len = L.plan.seg_len;
   for (auto &m : rs.dmask) m = ~0ull;
-  if (parts & 1)
+  if ((parts & kPartRows) && !(parts & kEarlyExit))
     launch_row_stats(dtype, false, rs, static_cast<int64_t>(B) * L.rows_per_seq * L.plan.S, part, stream);
-  if (!(parts & 2)) return launch_status();
+  if (!(parts & (kPartFinish | kEarlyExit))) return launch_status();
 
   WindowArgs A{};
   A.t = rs.t;
@@ -166,7 +175,28 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
   A.p_draft = p_draft;
   A.q_draft = q_draft;
   A.jobs = jobs;
-  launch_window_finish(dtype, A, B, reinterpret_cast<float *>(wsb + L.spart_off), L.cmax, stream);
+  float *spart = reinterpret_cast<float *>(wsb + L.spart_off);
+  if (!(parts & kEarlyExit)) {
+    launch_window_finish(dtype, A, B, spart, L.cmax, stream);
+    return launch_status();
+  }
+  // Position blocks [0,1), [1,3), [3,7), ... up to the bonus row gamma.  A
+  // row workgroup of a sequence that is already done exits at once.
+  int32_t *status = reinterpret_cast<int32_t *>(wsb + L.status_off);
+  for (int lo = 0, width = 1; lo <= gamma; lo += width, width *= 2) {
+    const int hi = std::min(gamma + 1, lo + width);
+    RowSet st = rs;
+    st.t0 = st.d0 = lo;
+    st.rows_t = hi - lo;
+    st.rows_d = std::max(0, std::min(hi, static_cast<int>(gamma)) - lo);
+    st.t_slot0 = lo;
+    st.d_slot0 = gamma + 1 + lo;
+    st.status = lo == 0 ? nullptr : status;
+    launch_row_stats(dtype, false, st, static_cast<int64_t>(B) * (st.rows_t + st.rows_d) * L.plan.S, part,
+                     stream);
+    launch_stage_decide(dtype, A, B, lo, hi, status, stream);
+  }
+  launch_tree_finish(dtype, jobs, B, V, spart, L.cmax, stream);
   return launch_status();
 }
 
@@ -183,9 +213,23 @@ int sv_verify_window(const void *target_logits, int64_t target_seq_stride,
                      int32_t *n_accepted, int32_t *out_tokens,
                      float *p_draft, float *q_draft,
                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  return window_impl(3, target_logits, target_seq_stride, draft_logits, draft_seq_stride, dtype,
+  return window_impl(kPartRows | kPartFinish, target_logits, target_seq_stride, draft_logits, draft_seq_stride, dtype,
                      draft_tokens, window_len, B, gamma, V, seed, tag, seq_ids, base_pos,
                      n_accepted, out_tokens, p_draft, q_draft, workspace, workspace_bytes, stream);
+}
+
+int sv_verify_window_early_exit(const void *target_logits, int64_t target_seq_stride,
+                                const void *draft_logits, int64_t draft_seq_stride, int dtype,
+                                const int32_t *draft_tokens, const int32_t *window_len,
+                                int32_t B, int32_t gamma, int32_t V,
+                                uint64_t seed, uint64_t tag, const uint64_t *seq_ids,
+                                const int64_t *base_pos,
+                                int32_t *n_accepted, int32_t *out_tokens,
+                                float *p_draft, float *q_draft,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return window_impl(kEarlyExit, target_logits, target_seq_stride, draft_logits, draft_seq_stride, dtype,
+                     draft_tokens, window_len, B, gamma, V, seed, tag, seq_ids, base_pos, n_accepted,
+                     out_tokens, p_draft, q_draft, workspace, workspace_bytes, stream);
 }
 
 int sv_verify_window_part(int part, const void *target_logits, int64_t target_seq_stride,
@@ -198,7 +242,7 @@ int sv_verify_window_part(int part, const void *target_logits, int64_t target_se
                           float *p_draft, float *q_draft,
                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
   if (part != SV_PART_ROW_STATS && part != SV_PART_DECIDE_SAMPLE) return SV_EINVAL;
-  return window_impl(part == SV_PART_ROW_STATS ? 1 : 2, target_logits, target_seq_stride,
+  return window_impl(part == SV_PART_ROW_STATS ? kPartRows : kPartFinish, target_logits, target_seq_stride,
                      draft_logits, draft_seq_stride, dtype, draft_tokens, window_len, B, gamma, V,
                      seed, tag, seq_ids, base_pos, n_accepted, out_tokens, p_draft, q_draft,
                      workspace, workspace_bytes, stream);
@@ -229,7 +273,12 @@ int sv_verify_greedy(const void *target_logits, int64_t target_seq_stride, int d
   rs.d = nullptr;
   rs.rows_t = gamma + 1;
   rs.rows_d = 0;
+  rs.t0 = rs.d0 = 0;
+  rs.R_out = gamma + 1;
+  rs.t_slot0 = 0;
+  rs.d_slot0 = gamma + 1;
   rs.window_len = window_len;
+  rs.status = nullptr;
   rs.gamma = gamma;
   rs.V = V;
   rs.S = L.plan.S;
@@ -289,7 +338,12 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
   rs.d_stride_bytes = seq_bytes;
   rs.rows_t = N;
   rs.rows_d = (mode == SV_TREE_STOCHASTIC) ? N : 0;
+  rs.t0 = rs.d0 = 0;
+  rs.R_out = 2 * N;
+  rs.t_slot0 = 0;
+  rs.d_slot0 = N;
   rs.window_len = nullptr;
+  rs.status = nullptr;
   rs.gamma = 0;
   rs.V = V;
   rs.S = L.plan.S;

@@ -133,20 +133,25 @@ __global__ void __launch_bounds__(kRowThreads) k_row_stats(RowSet rs, float2 *__
   const int j = static_cast<int>(rj % R);
   const int64_t b = rj / R;
 
+  if (rs.status && rs.status[b] != kSeqVerifying) return;
   int len = rs.gamma;
   if (rs.window_len) {
     len = rs.window_len[b];
     if (len < 0 || len > rs.gamma) return;
   }
   const char *row;
+  int slot;
   if (j < rs.rows_t) {
-    if (rs.window_len && j > len) return;
-    row = rs.t + b * rs.t_stride_bytes + static_cast<int64_t>(j) * rs.V * E::kBytes;
+    const int i = rs.t0 + j;
+    if (rs.window_len && i > len) return;
+    row = rs.t + b * rs.t_stride_bytes + static_cast<int64_t>(i) * rs.V * E::kBytes;
+    slot = rs.t_slot0 + j;
   } else {
-    const int jd = j - rs.rows_t;
-    if (rs.window_len && jd >= len) return;
-    if (!((rs.dmask[jd >> 6] >> (jd & 63)) & 1ull)) return;
-    row = rs.d + b * rs.d_stride_bytes + static_cast<int64_t>(jd) * rs.V * E::kBytes;
+    const int i = rs.d0 + (j - rs.rows_t);
+    if (rs.window_len && i >= len) return;
+    if (!((rs.dmask[i >> 6] >> (i & 63)) & 1ull)) return;
+    row = rs.d + b * rs.d_stride_bytes + static_cast<int64_t>(i) * rs.V * E::kBytes;
+    slot = rs.d_slot0 + (j - rs.rows_t);
   }
 
   const int lo = seg * rs.seg_len;
@@ -204,7 +209,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row_stats(RowSet rs, float2 *__
 
   __shared__ float lds_m[kRowThreads / kWave], lds_s[kRowThreads / kWave];
   const float2 res = acc.result(lds_m, lds_s, tid);
-  if (tid == 0) part[blk] = res;
+  if (tid == 0) part[(b * rs.R_out + slot) * rs.S + seg] = res;
 }
 
 // Combine the S segment results of one row, in segment order.
@@ -320,6 +325,107 @@ __device__ void window_decide(const WindowArgs &A, int b, int i, bool write, Sam
     jb.out_slot = out + n;
     *job = jb;
     if (write) A.n_accepted[b] = n;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decide: early-exit window, positions [lo, hi) of every sequence still
+// verifying (one wavefront per sequence, lane i <-> position lo + i)
+// ---------------------------------------------------------------------------
+// The first block (lo = 0) validates the sequence and sets its status; a
+// sequence is done at its first rejection (residual job on that row) or once
+// its window is exhausted (bonus job on row len), and then writes its outputs.
+// Row results, uniforms and the job are the ones sv_verify_window computes.
+template <int DT>
+__global__ void __launch_bounds__(kWave) k_stage_decide(WindowArgs A, int lo, int hi, int32_t *__restrict__ status) {
+  using E = Elt<DT>;
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const int p = lo + i;
+  const int R = 2 * A.gamma + 1;
+  int32_t *out = A.out_tokens + static_cast<int64_t>(b) * (A.gamma + 1);
+  if (lo > 0 && status[b] != kSeqVerifying) return;
+  const int len = A.window_len ? A.window_len[b] : A.gamma;
+  const int xp = p < A.gamma ? A.tokens[static_cast<int64_t>(b) * A.gamma + p] : 0;
+  if (lo == 0) {
+    const bool bad_len = len < 0 || len > A.gamma;
+    const bool bad_tok = !bad_len && p < len && (xp < 0 || xp >= A.V);
+    if (__any(bad_len || bad_tok)) {
+      for (int k = i; k <= A.gamma; k += kWave) out[k] = -1;
+      for (int k = i; k < A.gamma; k += kWave) {
+        if (A.p_draft) A.p_draft[static_cast<int64_t>(b) * A.gamma + k] = 0.0f;
+        if (A.q_draft) A.q_draft[static_cast<int64_t>(b) * A.gamma + k] = 0.0f;
+      }
+      if (i == 0) {
+        A.n_accepted[b] = -1;
+        A.jobs[b].mode = JOB_NONE;
+        status[b] = -1;
+      }
+      return;
+    }
+  }
+  const float2 *prow = A.part + static_cast<int64_t>(b) * R * A.S;
+  const char *trow0 = A.t + b * A.t_stride_bytes;
+  const char *drow0 = A.d + b * A.d_stride_bytes;
+  const int64_t row_bytes = static_cast<int64_t>(A.V) * E::kBytes;
+  const uint64_t seq = A.seq_ids ? A.seq_ids[b] : static_cast<uint64_t>(b);
+  const int64_t base = A.base_pos ? A.base_pos[b] : 0;
+  const int cnt = min(hi, len) - lo;  // positions examined in this block
+  MaxSum st{0.0f, 1.0f}, sd{0.0f, 1.0f};
+  if (p < hi) st = row_maxsum(prow + p * A.S, A.S);
+  if (p < hi && p < A.gamma) sd = row_maxsum(prow + (A.gamma + 1 + p) * A.S, A.S);
+  const U64x4 w = philox4x64_10({seq, static_cast<uint64_t>(base + 1 + p), 0, 0}, A.seed, A.tag);
+  const float vi = uniform24(w.c1);
+  float P = 0.0f, Q = 0.0f;
+  bool acc = false;
+  if (i < cnt) {
+    P = prob_at(E::one(trow0 + p * row_bytes, xp), st);
+    Q = prob_at(E::one(drow0 + p * row_bytes, xp), sd);
+    acc = uniform24(w.c0) * Q < P;
+  }
+  const uint64_t inv = ~static_cast<uint64_t>(__ballot(acc));
+  const int k = inv ? __builtin_ctzll(inv) : kWave;  // leading accepts in this block
+  const bool rejected = k < cnt;
+  const bool done = rejected || len < hi;
+  const int n = rejected ? lo + k : len;  // meaningful when done
+  if (i < cnt && (!done || p <= n)) {
+    const int64_t o = static_cast<int64_t>(b) * A.gamma + p;
+    if (A.p_draft) A.p_draft[o] = P;
+    if (A.q_draft) A.q_draft[o] = Q;
+  }
+  if (!done) {
+    if (i == 0 && lo == 0) status[b] = kSeqVerifying;
+    return;
+  }
+  for (int q = n + i; q < A.gamma; q += kWave) {  // never examined: past n or past the window
+    if (q == n && n < len) continue;
+    if (A.p_draft) A.p_draft[static_cast<int64_t>(b) * A.gamma + q] = 0.0f;
+    if (A.q_draft) A.q_draft[static_cast<int64_t>(b) * A.gamma + q] = 0.0f;
+  }
+  for (int q = i; q <= A.gamma; q += kWave)
+    if (q != n) out[q] = q < n ? A.tokens[static_cast<int64_t>(b) * A.gamma + q] : -1;
+  const int src = (n - lo) & (kWave - 1);
+  const MaxSum tn{__shfl(st.m, src), __shfl(st.s, src)};
+  const MaxSum dn{__shfl(sd.m, src), __shfl(sd.s, src)};
+  const float v = __shfl(vi, src);
+  if (i == 0) {
+    SampleJob jb{};
+    jb.t_row = trow0 + n * row_bytes;
+    jb.ct = norm_offset(tn);
+    if (rejected) {
+      jb.mode = JOB_RESIDUAL;
+      jb.d_row = drow0 + n * row_bytes;
+      jb.cd = norm_offset(dn);
+    } else {
+      jb.mode = JOB_BONUS;
+      jb.d_row = nullptr;
+      jb.cd = 0.0f;
+    }
+    jb.v = v;
+    jb.out_slot = out + n;
+    A.jobs[b] = jb;
+    A.n_accepted[b] = n;
+    status[b] = n;
   }
 }
 
@@ -894,6 +1000,14 @@ static void launch_finish(int dtype, const WindowArgs &A, SampleJob *jobs, int B
 
 void launch_window_finish(int dtype, const WindowArgs &A, int B, float *spart, int cmax, hipStream_t st) {
   launch_finish<true>(dtype, A, A.jobs, B, A.V, spart, cmax, st);
+}
+
+void launch_stage_decide(int dtype, const WindowArgs &A, int B, int lo, int hi, int32_t *status, hipStream_t st) {
+  switch (dtype) {
+    case DT_BF16: hipLaunchKernelGGL(k_stage_decide<DT_BF16>, dim3(B), dim3(kWave), 0, st, A, lo, hi, status); break;
+    case DT_F16: hipLaunchKernelGGL(k_stage_decide<DT_F16>, dim3(B), dim3(kWave), 0, st, A, lo, hi, status); break;
+    default: hipLaunchKernelGGL(k_stage_decide<DT_F32>, dim3(B), dim3(kWave), 0, st, A, lo, hi, status); break;
+  }
 }
 
 void launch_greedy_decide(const GreedyArgs &A, int B, hipStream_t st) {

@@ -78,7 +78,7 @@ struct Layout {
   RowPlan plan;
   int rows_per_seq;
   int cmax;  // chunk sums per sequence in the split draw
-  size_t part_off, jobs_off, spart_off, total;
+  size_t part_off, jobs_off, spart_off, status_off, total;
 };
 
 // op: 0 window, 1 greedy, 2 tree (n = gamma or N).
@@ -96,6 +96,8 @@ inline Layout make_layout(int op, int64_t B, int32_t n, int32_t V) {
   L.cmax = (op == 1) ? 0 : (V + kFinThreads * 4 - 1) / (kFinThreads * 4);
   L.spart_off = off;
   off = align256(off + sizeof(float) * static_cast<size_t>(B) * L.cmax);
+  L.status_off = off;  // early-exit window: per-sequence status
+  off = align256(off + (op == 0 ? sizeof(int32_t) * static_cast<size_t>(B) : 0));
   L.total = off;
   return L;
 }

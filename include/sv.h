@@ -132,6 +132,25 @@ int sv_verify_window_part(int part, const void *target_logits, int64_t target_se
                           float *p_draft, float *q_draft,
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* sv_verify_window that stops reading a sequence's rows at its first
+ * rejection ("the scan stops at the first rejection"): target and draft rows
+ * are reduced in position blocks [0,1), [1,3), [3,7), ..., each followed by a
+ * decision; a sequence that has rejected a draft (or used up its window) reads
+ * no further rows.  Same arguments and workspace (SV_OP_WINDOW) as
+ * sv_verify_window; n_accepted and out_tokens are bit-identical to it, as are
+ * p_draft/q_draft for i <= n (they are 0 past n).  The row bytes read shrink
+ * from B(2 gamma + 1)V to about B(2 E[n] + 2)V at the cost of 2 launches per
+ * block (4 blocks at gamma = 8). */
+int sv_verify_window_early_exit(const void *target_logits, int64_t target_seq_stride,
+                                const void *draft_logits, int64_t draft_seq_stride, int dtype,
+                                const int32_t *draft_tokens, const int32_t *window_len,
+                                int32_t B, int32_t gamma, int32_t V,
+                                uint64_t seed, uint64_t tag, const uint64_t *seq_ids,
+                                const int64_t *base_pos,
+                                int32_t *n_accepted, int32_t *out_tokens,
+                                float *p_draft, float *q_draft,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Greedy window verification (temperature 0).  Same layouts as
  * sv_verify_window; only target rows 0..window_len are read.  n is the first
  * i < len with draft_tokens[i] != argmax(row i) (smallest index among equal
