@@ -151,10 +151,6 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
   rs.S = L.plan.S;
   rs.seg_len = L.plan.seg_len;
   for (auto &m : rs.dmask) m = ~0ull;
-  if ((parts & kPartRows) && !(parts & kEarlyExit))
-    launch_row_stats(dtype, false, rs, static_cast<int64_t>(B) * L.rows_per_seq * L.plan.S, part, stream);
-  if (!(parts & (kPartFinish | kEarlyExit))) return launch_status();
-
   WindowArgs A{};
   A.t = rs.t;
   A.t_stride_bytes = rs.t_stride_bytes;
@@ -175,6 +171,9 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
   A.p_draft = p_draft;
   A.q_draft = q_draft;
   A.jobs = jobs;
+  if ((parts & kPartRows) && !(parts & kEarlyExit))
+    launch_row_stats(dtype, false, rs, static_cast<int64_t>(B) * L.rows_per_seq * L.plan.S, part, stream);
+  if (!(parts & (kPartFinish | kEarlyExit))) return launch_status();
   float *spart = reinterpret_cast<float *>(wsb + L.spart_off);
   if (!(parts & kEarlyExit)) {
     launch_window_finish(dtype, A, B, spart, L.cmax, stream);

@@ -35,16 +35,16 @@ constexpr int kUnroll = SV_ROW_UNROLL;
 // Pass 1: row statistics
 // ---------------------------------------------------------------------------
 
-template <int DT, bool kArgmax>
+template <int DT, bool kArgmax, int U = kUnroll>
 struct RowAcc;
 
-template <int DT>
-struct RowAcc<DT, false> {
+template <int DT, int U>
+struct RowAcc<DT, false, U> {
   float m = kNegInf, s = 0.0f;
   __device__ __forceinline__ void batch(const float *x, int n, int) {
     float bm = x[0];
 #pragma unroll
-    for (int k = 1; k < kUnroll * Elt<DT>::kEPV; ++k) bm = fmaxf(bm, x[k]);
+    for (int k = 1; k < U * Elt<DT>::kEPV; ++k) bm = fmaxf(bm, x[k]);
     if (bm > m) {
       s *= rescale(m, bm);
       m = bm;
@@ -53,7 +53,7 @@ struct RowAcc<DT, false> {
       const float ml = m * kLog2e;
       float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int k = 0; k < kUnroll * Elt<DT>::kEPV; ++k) acc[k & 3] += exp_shift(x[k], ml);
+      for (int k = 0; k < U * Elt<DT>::kEPV; ++k) acc[k & 3] += exp_shift(x[k], ml);
       s += (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
     (void)n;
@@ -81,20 +81,20 @@ struct RowAcc<DT, false> {
   }
 };
 
-template <int DT>
-struct RowAcc<DT, true> {
+template <int DT, int U>
+struct RowAcc<DT, true, U> {
   float m = kNegInf;
   int i = INT_MAX;
-  // x holds kUnroll vectors; vector u starts at element index base + u * stride.
+  // x holds U vectors; vector u starts at element index base + u * stride.
   __device__ __forceinline__ void batch(const float *x, int base, int stride) {
     constexpr int EPV = Elt<DT>::kEPV;
     float bm = x[0];
 #pragma unroll
-    for (int k = 1; k < kUnroll * EPV; ++k) bm = fmaxf(bm, x[k]);
+    for (int k = 1; k < U * EPV; ++k) bm = fmaxf(bm, x[k]);
     if (bm > m) {
       int found = INT_MAX;
 #pragma unroll
-      for (int k = kUnroll * EPV - 1; k >= 0; --k)
+      for (int k = U * EPV - 1; k >= 0; --k)
         if (x[k] == bm) found = base + (k / EPV) * stride + (k % EPV);
       m = bm;
       i = found;
@@ -122,10 +122,65 @@ struct RowAcc<DT, true> {
   }
 };
 
+// Streams elements [lo, hi) of one row into a per-thread accumulator: a
+// scalar head up to the first 16-byte boundary, a body of 16-byte vectors,
+// a scalar tail.  Body vectors go in batches of U per thread (thread tid takes
+// vectors tid, tid + NT, ...); over full batches the next batch's loads are in
+// flight while the current batch is reduced, and a guarded remainder batch
+// fills its gaps with -inf.
+template <int DT, int NT, int U, typename Acc>
+__device__ __forceinline__ void stream_segment(const char *row, int lo, int hi, int tid, Acc &acc) {
+  using E = Elt<DT>;
+  constexpr int EPV = E::kEPV;
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(row + static_cast<int64_t>(lo) * E::kBytes);
+  const int mis = static_cast<int>(addr & 15);
+  const int head = min(mis ? (16 - mis) / E::kBytes : 0, hi - lo);
+  const int a = lo + head;
+  const int nvec = (hi - a) / EPV;
+  const int tail = a + nvec * EPV;
+  const uint4 *vp = reinterpret_cast<const uint4 *>(row + static_cast<int64_t>(a) * E::kBytes);
+  constexpr int kStep = U * NT;
+  const int nfull = nvec / kStep;
+  if (nfull > 0) {
+    uint4 cur[U], nxt[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = load_stream(vp + u * NT + tid);
+    for (int it = 0; it < nfull - 1; ++it) {
+      const uint4 *q = vp + (it + 1) * kStep + tid;
+#pragma unroll
+      for (int u = 0; u < U; ++u) nxt[u] = load_stream(q + u * NT);
+      float x[U * EPV];
+#pragma unroll
+      for (int u = 0; u < U; ++u) E::vec(cur[u], x + u * EPV);
+      acc.batch(x, a + (it * kStep + tid) * EPV, NT * EPV);
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    }
+    float x[U * EPV];
+#pragma unroll
+    for (int u = 0; u < U; ++u) E::vec(cur[u], x + u * EPV);
+    acc.batch(x, a + ((nfull - 1) * kStep + tid) * EPV, NT * EPV);
+  }
+  if (nfull * kStep < nvec) {
+    const uint4 neg = make_uint4(E::kNegInfPair, E::kNegInfPair, E::kNegInfPair, E::kNegInfPair);
+    uint4 r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int vi = nfull * kStep + u * NT + tid;
+      r[u] = vi < nvec ? load_stream(vp + vi) : neg;
+    }
+    float x[U * EPV];
+#pragma unroll
+    for (int u = 0; u < U; ++u) E::vec(r[u], x + u * EPV);
+    acc.batch(x, a + (nfull * kStep + tid) * EPV, NT * EPV);
+  }
+  for (int k = lo + tid; k < a; k += NT) acc.one(E::one(row, k), k);
+  for (int k = tail + tid; k < hi; k += NT) acc.one(E::one(row, k), k);
+}
+
 template <int DT, bool kArgmax>
 __global__ void __launch_bounds__(kRowThreads) k_row_stats(RowSet rs, float2 *__restrict__ part) {
   using E = Elt<DT>;
-  constexpr int EPV = E::kEPV;
   const uint32_t R = rs.rows_t + rs.rows_d;
   const uint32_t blk = blockIdx.x;  // B * R * S < 2^31 (checked on the host)
   const int seg = static_cast<int>(blk % static_cast<uint32_t>(rs.S));
@@ -156,56 +211,9 @@ __global__ void __launch_bounds__(kRowThreads) k_row_stats(RowSet rs, float2 *__
 
   const int lo = seg * rs.seg_len;
   const int hi = min(rs.V, lo + rs.seg_len);
-  const uintptr_t addr = reinterpret_cast<uintptr_t>(row + static_cast<int64_t>(lo) * E::kBytes);
-  const int mis = static_cast<int>(addr & 15);
-  const int head = min(mis ? (16 - mis) / E::kBytes : 0, hi - lo);
-  const int a = lo + head;
-  const int nvec = (hi - a) / EPV;
-  const int tail = a + nvec * EPV;
-  const uint4 *vp = reinterpret_cast<const uint4 *>(row + static_cast<int64_t>(a) * E::kBytes);
   const int tid = threadIdx.x;
-
   RowAcc<DT, kArgmax> acc;
-  // Full batches: every load in range, no per-lane guards, so the next batch's
-  // loads stay in flight while the current batch is reduced.
-  constexpr int kStep = kUnroll * kRowThreads;
-  const int nfull = nvec / kStep;
-  if (nfull > 0) {
-    uint4 cur[kUnroll], nxt[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) cur[u] = load_stream(vp + u * kRowThreads + tid);
-    for (int it = 0; it < nfull - 1; ++it) {
-      const uint4 *q = vp + (it + 1) * kStep + tid;
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) nxt[u] = load_stream(q + u * kRowThreads);
-      float x[kUnroll * EPV];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) E::vec(cur[u], x + u * EPV);
-      acc.batch(x, a + (it * kStep + tid) * EPV, kRowThreads * EPV);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
-    }
-    float x[kUnroll * EPV];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) E::vec(cur[u], x + u * EPV);
-    acc.batch(x, a + ((nfull - 1) * kStep + tid) * EPV, kRowThreads * EPV);
-  }
-  // Remainder batch (fewer than kStep vectors), guarded; -inf fills the gaps.
-  if (nfull * kStep < nvec) {
-    const uint4 neg = make_uint4(E::kNegInfPair, E::kNegInfPair, E::kNegInfPair, E::kNegInfPair);
-    uint4 r[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int vi = nfull * kStep + u * kRowThreads + tid;
-      r[u] = vi < nvec ? load_stream(vp + vi) : neg;
-    }
-    float x[kUnroll * EPV];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) E::vec(r[u], x + u * EPV);
-    acc.batch(x, a + (nfull * kStep + tid) * EPV, kRowThreads * EPV);
-  }
-  for (int k = lo + tid; k < a; k += kRowThreads) acc.one(E::one(row, k), k);
-  for (int k = tail + tid; k < hi; k += kRowThreads) acc.one(E::one(row, k), k);
+  stream_segment<DT, kRowThreads, kUnroll>(row, lo, hi, tid, acc);
 
   __shared__ float lds_m[kRowThreads / kWave], lds_s[kRowThreads / kWave];
   const float2 res = acc.result(lds_m, lds_s, tid);

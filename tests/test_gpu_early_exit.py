@@ -83,3 +83,28 @@ def test_early_exit_strided_inputs_and_seq_ids():
     bp = torch.arange(B, dtype=torch.int64, device=DEV) * 3
     res = _same_as_full_window(d, seed=4, seq_ids=sid, base_pos=bp)
     check_window(d, res, seed=4, seq_ids=sid, base_pos=bp)
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 1003), ("f16", 50257), ("f32", 2049)])
+def test_large_batch_ragged_rows_and_partial_windows(dtype, V):
+    # B = 256 takes the one-workgroup-per-sequence kernel on a 256-CU device;
+    # rows here start off 16-byte boundaries and windows are partial
+    B, gamma = 256, 7
+    d = synth.window_batch(B, gamma, V, dtype, target_sd=2.0, boost=3.0, sigma=0.5, seed=91,
+                           device=DEV)
+    wl = torch.tensor([b % (gamma + 1) for b in range(B)], dtype=torch.int32, device=DEV)
+    wl[9] = -1
+    res = _same_as_full_window(d, seed=8, window_len=wl)
+    rows = [b for b in range(0, B, 9) if b != 9]
+    n, m = check_window(d, res, seed=8, window_len=wl, rows=rows)
+    assert m <= 1 and res.n_accepted[9].item() == -1
+    # the two-kernel form of the same call, through the split entry point
+    ws = sv.workspace(sv.SV_OP_WINDOW, B, gamma, V, d["target"].dtype, DEV)
+    two = sv.WindowResult(torch.empty(B, dtype=torch.int32, device=DEV),
+                          torch.empty(B, gamma + 1, dtype=torch.int32, device=DEV),
+                          torch.empty(B, gamma, device=DEV), torch.empty(B, gamma, device=DEV))
+    for part in (sv.api.SV_PART_ROW_STATS, sv.api.SV_PART_DECIDE_SAMPLE):
+        sv.verify_window(d["target"], d["draft"], d["tokens"], seed=8, window_len=wl, ws=ws,
+                         out=two, part=part)
+    n, m = check_window(d, two, seed=8, window_len=wl, rows=rows)
+    assert m <= 1
