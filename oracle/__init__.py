@@ -36,6 +36,7 @@ from .verify import (
     verify_greedy,
     tree_meta,
     verify_tree,
+    verify_tree_multiround,
     rollback,
     hierarchy_three_stage,
 )
@@ -53,6 +54,7 @@ __all__ = [
     "verify_greedy",
     "tree_meta",
     "verify_tree",
+    "verify_tree_multiround",
     "rollback",
     "hierarchy_three_stage",
 ]

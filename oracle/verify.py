@@ -29,6 +29,8 @@ Readings where the pages are silent (each listed in the design doc):
 * a tree node is accepted when its own test passes against its parent's row
   and its parent is accepted; the deepest accepted node wins, ties to the
   smallest node index;
+* the lossless tree walk (verify_tree_multiround) tries siblings in index
+  order, and after a rejection whose residual has no mass keeps the residual;
 * rollback keeps a buffer that already agrees with the verified sequence and
   is at least as long, otherwise truncates it at the first divergence and
   appends the verified tail.
@@ -36,7 +38,10 @@ Readings where the pages are silent (each listed in the design doc):
 Pins: tests/test_oracle_*.py (brute-force exact laws at V=8, chi-square on
 Philox-driven windows, the pages' expected-length and steady-state formulas on
 exact-alpha inputs, scipy softmax/logsumexp, numpy argmax, special cases,
-chain tree == window, brute-force tree paths, rollback invariants).
+chain tree == window, brute-force tree paths, rollback invariants; for the
+multi-candidate walk: its exact output law equals the target's autoregressive
+law on enumerated small trees, chain == window, and the closed form of the
+residual after j rejections).
 """
 
 import numpy as np
@@ -284,6 +289,97 @@ def verify_tree(target, draft, node_tokens, parent, mode, u_node, v_node):
         "path": path,
         "out": [int(node_tokens[v]) for v in path] + [int(y)],
         "ok": ok,
+        "sample": sample,
+    }
+
+
+# --------------------------------------------------------------------------
+# token tree, lossless multi-candidate walk
+# --------------------------------------------------------------------------
+
+
+def verify_tree_multiround(target, draft, node_tokens, parent, u_node, v_node):
+    """Multi-candidate tree verification that keeps the target distribution.
+
+    The pages cite this family only by title: SpecInfer, "tree-based
+    speculative inference and verification" (PipeSpec review page, reference
+    [16]; CLaSp review page, reference [29]).  This is that paper's published
+    multi-round scheme, restated for one draft model whose sibling tokens are
+    i.i.d. draws from the parent's draft row:
+
+    Start at the root with r = p_w (w = current node).  Try the children of w
+    in index order; child c with token x is accepted when u_c * q_w(x) < r(x)
+    (u < min(1, r/q), strict as in the window).  On a rejection the residual
+    becomes r <- max(0, r - q_w) / sum(max(0, r - q_w)); if that sum is 0 (only
+    possible when r equals q_w) r is kept.  An accepted child becomes the new
+    w and r restarts at its own p.  The walk ends at a leaf (bonus draw from
+    p_w with v_w) or when every child of w was rejected (draw from r with v_w).
+
+    Arguments as in verify_tree.  Returns n (depth of the final node), best
+    (the final node), path, out (path tokens then the drawn token), tests (one
+    record per sibling test: node, parent, u, ratio r(x)/q(x), r(x), q(x),
+    the product `mass` of the normalisers applied to r so far and `shift`, the
+    accumulated q-mass subtracted), and the sample record with the weights the
+    final token was drawn from.
+    """
+    N = len(parent)
+    depth, rank, has_child = tree_meta(parent)
+    V = target.shape[1]
+    for v in range(1, N):
+        if not (0 <= int(node_tokens[v]) < V):
+            raise ValueError("node token outside the vocabulary")
+    children = [[] for _ in range(N)]
+    for v in range(1, N):
+        children[parent[v]].append(v)
+
+    tests = []
+    path = []
+    w = 0
+    while True:
+        p_w = softmax(target[w])
+        r = p_w
+        mass, shift = 1.0, 0.0  # r == max(0, p_w - shift * q_w) / mass
+        accepted = None
+        if has_child[w]:
+            q_w = softmax(draft[w])
+            for c in children[w]:
+                x = int(node_tokens[c])
+                rx, qx = float(r[x]), float(q_w[x])
+                tests.append({"node": c, "parent": w, "u": u_node[c],
+                              "ratio": rx / qx if qx > 0 else np.inf,
+                              "r": rx, "q": qx, "p": float(p_w[x]),
+                              "mass": mass, "shift": shift})
+                if u_node[c] * qx < rx:
+                    accepted = c
+                    break
+                resid = np.maximum(0.0, r - q_w)
+                z = float(resid.sum())
+                if z > 0.0:
+                    r = resid / z
+                    shift += mass
+                    mass *= z
+        if accepted is None:
+            break
+        path.append(accepted)
+        w = accepted
+
+    y, info = inverse_cdf(r, v_node[w])
+    if not has_child[w]:
+        kind = "bonus"
+    elif r is p_w:
+        kind = "residual-empty"
+    else:
+        kind = "residual"
+    sample = dict(info)
+    sample["kind"] = kind
+    sample["y"] = int(y)
+    sample["weights"] = r
+    return {
+        "n": depth[w],
+        "best": w,
+        "path": path,
+        "out": [int(node_tokens[v]) for v in path] + [int(y)],
+        "tests": tests,
         "sample": sample,
     }
 
