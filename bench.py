@@ -335,10 +335,20 @@ def side_workloads(torch, sv, synth, dev):
     # tree (4, 3, 2), B=4, V=50257 fp16
     d = synth.tree_config3(device=dev)
     w = sv.workspace(sv.SV_OP_TREE, 4, 41, 50257, torch.float16, dev)
-    for mode in ("greedy", "stochastic"):
+    for mode in ("greedy", "stochastic", "multi_candidate"):
         ms = event_time_ms(torch, lambda: sv.verify_tree(d["target"], d["draft"], d["tokens"], d["parent"],
                                                          mode=mode, ws=w), reps)
         out[f"tree_432_B4_V50257_f16_{mode}"] = {"us": ms * 1e3}
+    # the multi-candidate walk with frequent sibling rejections (draft noise sd 2)
+    d = synth.tree_batch(32, synth.bfs_tree((4, 3, 2)), 50257, dtype="f16", sigma=2.0, seed=1013,
+                         device=dev)
+    w = sv.workspace(sv.SV_OP_TREE, 32, 41, 50257, torch.float16, dev)
+    ms = event_time_ms(torch, lambda: sv.verify_tree(d["target"], d["draft"], d["tokens"], d["parent"],
+                                                     mode="multi_candidate", ws=w), reps)
+    r = sv.verify_tree(d["target"], d["draft"], d["tokens"], d["parent"], mode="multi_candidate", ws=w)
+    out["tree_432_B32_V50257_f16_sigma2_multi_candidate"] = {
+        "us": ms * 1e3, "mean_depth": float(r.n_accepted.float().mean().item())}
+    del d, w
 
     # PipeSpec-shaped hierarchy, 64 streams: stage-1 window, rollback, stage-2 window, rollback
     h = synth.hierarchy_config4(S=64, mode="stochastic", device=dev)

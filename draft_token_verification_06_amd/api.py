@@ -13,7 +13,9 @@ import torch
 from ._lib import lib
 
 SV_OP_WINDOW, SV_OP_GREEDY, SV_OP_TREE = 0, 1, 2
-SV_TREE_GREEDY, SV_TREE_STOCHASTIC = 0, 1
+SV_TREE_GREEDY, SV_TREE_STOCHASTIC, SV_TREE_MULTI_CANDIDATE = 0, 1, 2
+_TREE_MODES = {"greedy": SV_TREE_GREEDY, "stochastic": SV_TREE_STOCHASTIC,
+               "multi_candidate": SV_TREE_MULTI_CANDIDATE}
 _DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
 
@@ -163,17 +165,21 @@ def tree_max_depth(parent):
 
 def verify_tree(target, draft, node_tokens, parent, *, mode="stochastic", seed=0, tag=0,
                 seq_ids=None, base_pos=None, ws=None):
-    """Token-tree verification: sv_verify_tree.  parent is a host sequence."""
+    """Token-tree verification: sv_verify_tree.  parent is a host sequence;
+    mode "greedy", "stochastic" or "multi_candidate"."""
     B, N, V = target.shape
     if len(parent) != N:
         raise ValueError("parent must have one entry per tree node")
     if target.stride(2) != 1 or target.stride(1) != V or target.stride(0) != N * V:
         raise ValueError("target must be contiguous (B, N, V)")
-    code = SV_TREE_STOCHASTIC if mode == "stochastic" else SV_TREE_GREEDY
-    if code == SV_TREE_STOCHASTIC:
+    if mode not in _TREE_MODES:
+        raise ValueError(f"unknown tree mode {mode!r}")
+    code = _TREE_MODES[mode]
+    sampled = code != SV_TREE_GREEDY
+    if sampled:
         if draft is None or draft.shape != target.shape or draft.dtype != target.dtype \
                 or not draft.is_contiguous():
-            raise ValueError("stochastic mode needs contiguous draft logits shaped like target")
+            raise ValueError("sampled modes need contiguous draft logits shaped like target")
     _i32(node_tokens, (B, N), "node_tokens")
     _optional(seq_ids, torch.int64, B, "seq_ids")
     _optional(base_pos, torch.int64, B, "base_pos")
@@ -188,7 +194,7 @@ def verify_tree(target, draft, node_tokens, parent, *, mode="stochastic", seed=0
     par = (ctypes.c_int32 * N)(*parent)
     with torch.cuda.device(dev):
         _check(lib().sv_verify_tree(
-            _ptr(target), _ptr(draft if code == SV_TREE_STOCHASTIC else None),
+            _ptr(target), _ptr(draft if sampled else None),
             _DTYPE_CODE[target.dtype], _ptr(node_tokens), par, B, N, V, code,
             ctypes.c_uint64(seed), ctypes.c_uint64(tag), _ptr(seq_ids), _ptr(base_pos),
             _ptr(res.n_accepted), _ptr(res.best_node), _ptr(res.out_tokens), _ptr(res.out_nodes),

@@ -51,6 +51,12 @@ int build_tree(const int32_t *parent, int32_t N, TreeMeta *meta) {
   int count_at[kTreeMaxNodes + 1] = {0};
   count_at[0] = 1;
   meta->parent[0] = -1;
+  int last_child[kTreeMaxNodes];
+  for (int v = 0; v < kTreeMaxNodes; ++v) {
+    meta->first_child[v] = -1;
+    meta->next_sibling[v] = -1;
+    last_child[v] = -1;
+  }
   int max_depth = 0;
   for (int v = 1; v < N; ++v) {
     const int w = parent[v];
@@ -61,6 +67,9 @@ int build_tree(const int32_t *parent, int32_t N, TreeMeta *meta) {
     meta->depth[v] = static_cast<uint8_t>(d);
     meta->rank[v] = static_cast<int16_t>(count_at[d]++);
     meta->internal[w >> 6] |= 1ull << (w & 63);
+    if (last_child[w] < 0) meta->first_child[w] = static_cast<int16_t>(v);
+    else meta->next_sibling[last_child[w]] = static_cast<int16_t>(v);
+    last_child[w] = v;
     if (d > max_depth) max_depth = d;
   }
   meta->max_depth = max_depth;
@@ -313,13 +322,15 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
   const int eb = elem_bytes(dtype);
   if (eb == 0) return SV_EDTYPE;
-  if (B < 1 || V < 1 || V > kMaxVocab || (mode != SV_TREE_GREEDY && mode != SV_TREE_STOCHASTIC)) return SV_EINVAL;
+  if (B < 1 || V < 1 || V > kMaxVocab) return SV_EINVAL;
+  if (mode != SV_TREE_GREEDY && mode != SV_TREE_STOCHASTIC && mode != SV_TREE_MULTI_CANDIDATE) return SV_EINVAL;
+  const bool sampled = mode != SV_TREE_GREEDY;
   TreeMeta meta;
   const int tst = build_tree(parent_host, N, &meta);
   if (tst != SV_OK) return tst;
   if (!target_logits || !node_tokens || !n_accepted || !best_node || !out_tokens) return SV_EINVAL;
   if (meta.max_depth > 0 && !out_nodes) return SV_EINVAL;
-  if (mode == SV_TREE_STOCHASTIC && !draft_logits) return SV_EINVAL;
+  if (sampled && !draft_logits) return SV_EINVAL;
   if (!aligned(target_logits, eb) || (draft_logits && !aligned(draft_logits, eb))) return SV_EINVAL;
   const Layout L = make_layout(SV_OP_TREE, B, N, V);
   if (!grid_fits(B, L)) return SV_EINVAL;
@@ -336,7 +347,7 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
   rs.d = static_cast<const char *>(draft_logits);
   rs.d_stride_bytes = seq_bytes;
   rs.rows_t = N;
-  rs.rows_d = (mode == SV_TREE_STOCHASTIC) ? N : 0;
+  rs.rows_d = sampled ? N : 0;
   rs.t0 = rs.d0 = 0;
   rs.R_out = 2 * N;
   rs.t_slot0 = 0;
@@ -351,7 +362,7 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
   // The plan is laid out for 2N rows per sequence; greedy launches only the
   // first N of them (target rows) but keeps the same partial-row indexing.
   const int R = 2 * N;
-  if (mode == SV_TREE_STOCHASTIC) {
+  if (sampled) {
     launch_row_stats(dtype, false, rs, static_cast<int64_t>(B) * R * L.plan.S, part, stream);
   } else {
     RowSet g = rs;
@@ -368,7 +379,7 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
   A.V = V;
   A.S = L.plan.S;
   A.R = R;
-  A.mode = mode == SV_TREE_STOCHASTIC ? 1 : 0;
+  A.mode = sampled ? 1 : 0;
   A.seed = seed;
   A.tag = tag;
   A.seq_ids = seq_ids;
@@ -380,6 +391,10 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
   A.out_nodes = out_nodes;
   A.jobs = jobs;
   A.meta = meta;
+  if (mode == SV_TREE_MULTI_CANDIDATE) {
+    launch_tree_walk(dtype, A, B, stream);
+    return launch_status();
+  }
   launch_tree_decide(dtype, A, B, stream);
   if (mode == SV_TREE_STOCHASTIC)
     launch_tree_finish(dtype, jobs, B, V, reinterpret_cast<float *>(wsb + L.spart_off), L.cmax, stream);

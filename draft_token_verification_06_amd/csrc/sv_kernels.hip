@@ -322,6 +322,7 @@ __device__ void window_decide(const WindowArgs &A, int b, int i, bool write, Sam
     jb.ct = norm_offset(tn);
     if (n < len) {
       jb.mode = JOB_RESIDUAL;
+      jb.cq = 1.0f;
       jb.d_row = drow0 + n * row_bytes;
       jb.cd = norm_offset(dn);
     } else {
@@ -422,6 +423,7 @@ __global__ void __launch_bounds__(kWave) k_stage_decide(WindowArgs A, int lo, in
     jb.ct = norm_offset(tn);
     if (rejected) {
       jb.mode = JOB_RESIDUAL;
+      jb.cq = 1.0f;
       jb.d_row = drow0 + n * row_bytes;
       jb.cd = norm_offset(dn);
     } else {
@@ -503,8 +505,9 @@ __global__ void __launch_bounds__(kTreeMaxNodes) k_tree_decide(TreeArgs A) {
   const int64_t base = A.base_pos ? A.base_pos[b] : 0;
 
   __shared__ unsigned char s_acc[kTreeMaxNodes];
+  __shared__ int s_parent[kTreeMaxNodes];
   __shared__ int s_path[kTreeMaxDepth + 1];
-  __shared__ int s_best;
+  __shared__ int s_best, s_key;
   if (v < N) {
     bool acc = true;
     if (v >= 1) {
@@ -523,19 +526,24 @@ __global__ void __launch_bounds__(kTreeMaxNodes) k_tree_decide(TreeArgs A) {
       }
     }
     s_acc[v] = acc;
+    s_parent[v] = A.meta.parent[v];
+  }
+  if (v == 0) s_key = 0;
+  __syncthreads();
+  // A node is accepted when its own test and every ancestor's passed; the
+  // deepest accepted node wins, ties to the smallest index (key depth, -index).
+  if (v < N) {
+    bool ok = s_acc[v];
+    for (int u = s_parent[v]; ok && u > 0; u = s_parent[u]) ok = s_acc[u];
+    if (ok) atomicMax(&s_key, (static_cast<int>(A.meta.depth[v]) << 16) | (0xFFFF - v));
   }
   __syncthreads();
   if (v == 0) {
-    // accepted = own test and parent accepted; nodes come after their parents
-    int best = 0;
-    for (int u = 1; u < N; ++u) {
-      s_acc[u] = s_acc[u] && s_acc[A.meta.parent[u]];
-      if (s_acc[u] && A.meta.depth[u] > A.meta.depth[best]) best = u;
-    }
+    const int best = 0xFFFF - (s_key & 0xFFFF);
     int w = best;
     for (int k = A.meta.depth[best] - 1; k >= 0; --k) {
       s_path[k] = w;
-      w = A.meta.parent[w];
+      w = s_parent[w];
     }
     s_best = best;
   }
@@ -556,6 +564,7 @@ __global__ void __launch_bounds__(kTreeMaxNodes) k_tree_decide(TreeArgs A) {
       job.ct = norm_offset(row_maxsum(prow + best * A.S, A.S));
       if ((A.meta.internal[best >> 6] >> (best & 63)) & 1ull) {
         job.mode = JOB_RESIDUAL;
+        job.cq = 1.0f;
         job.d_row = d0 + best * row_bytes;
         job.cd = norm_offset(row_maxsum(prow + (N + best) * A.S, A.S));
       } else {
@@ -576,48 +585,81 @@ __global__ void __launch_bounds__(kTreeMaxNodes) k_tree_decide(TreeArgs A) {
 // ---------------------------------------------------------------------------
 // Sampling pass: one 1024-thread workgroup per sequence
 // ---------------------------------------------------------------------------
-// Weight of token k: p_k (bonus) or max(0, p_k - q_k) (residual), with
+// Weight of token k: p_k (bonus) or max(0, p_k - cq q_k) (residual), with
 // p_k = 2^(t_k log2e - ct), q_k = 2^(d_k log2e - cd).
-// p_k, q_k <= 1, so max(0, p - q) is p - q clamped to [0, 1] (one instruction).
+// p_k <= 1 and cq >= 0, so the clamp to [0, 1] is the max (one instruction);
+// with cq = 1 the fused multiply-add rounds exactly like p - q.
 __device__ __forceinline__ float weight_of(const SampleJob &job, float t, float d) {
   const float p = exp2_fast(__builtin_fmaf(t, kLog2e, -job.ct));
   if (job.mode != JOB_RESIDUAL) return p;
-  return __builtin_amdgcn_fmed3f(p - exp2_fast(__builtin_fmaf(d, kLog2e, -job.cd)), 0.0f, 1.0f);
+  const float q = exp2_fast(__builtin_fmaf(d, kLog2e, -job.cd));
+  return __builtin_amdgcn_fmed3f(__builtin_fmaf(-job.cq, q, p), 0.0f, 1.0f);
 }
 
-// Both rows of the job start on a 16-byte boundary.
-__device__ __forceinline__ bool job_rows_aligned(const SampleJob &job) {
-  const bool ta = (reinterpret_cast<uintptr_t>(job.t_row) & 15) == 0;
-  const bool da = job.mode != JOB_RESIDUAL || (reinterpret_cast<uintptr_t>(job.d_row) & 15) == 0;
-  return ta && da;
+// Geometry of a sampling pass.  Vector geometry (kVec): the row is covered by
+// the 16-byte blocks that hold it, counted from the block holding element 0;
+// h = the offset of element 0 in its block, in elements (0 for aligned rows).
+// Both rows of a residual job must share h.  Element k of the row is slot
+// (k + h) % EPV of block (k + h) / EPV, so chunk c, thread t holds the EPV
+// elements [c CH + t EPV - h, ... + EPV) (CH = kFinThreads EPV); slots outside
+// [0, V) weigh 0.  A 16-byte aligned block never straddles a page, so loading
+// one that holds at least one element of the row is safe; blocks holding none
+// are not loaded.  Element geometry (!kVec, rows at different offsets): thread
+// t holds 4 elements [c CH + 4t, ... + 4), loaded one by one.
+__device__ __forceinline__ int job_shift(const SampleJob &job, int elem_bytes) {
+  const int ta = static_cast<int>(reinterpret_cast<uintptr_t>(job.t_row) & 15);
+  if (job.mode == JOB_RESIDUAL && static_cast<int>(reinterpret_cast<uintptr_t>(job.d_row) & 15) != ta) return -1;
+  return ta / elem_bytes;
 }
 
-// The row is cut into chunks of kFinThreads * E elements; thread t owns the E
-// contiguous elements [c*CH + t*E, c*CH + (t+1)*E) of chunk c (E = 8 bf16/f16
-// or 4 f32 with 16-byte loads, E = 4 with element loads for unaligned rows),
-// so one chunk is one coalesced sweep of the workgroup.
 template <int DT, bool kVec>
 struct FinGeom {
   static constexpr int E = kVec ? Elt<DT>::kEPV : 4;
   static constexpr int CH = kFinThreads * E;
 };
 
-// Weights of thread tid's elements of chunk c (0 past V).
 template <int DT, bool kVec>
-__device__ __forceinline__ void thread_weights(const SampleJob &job, int V, int c, int tid, float *w) {
+__device__ __forceinline__ int finish_chunks(int V, int h) {
+  return (V + h + FinGeom<DT, kVec>::CH - 1) / FinGeom<DT, kVec>::CH;
+}
+
+// First element index of thread tid's slots in chunk c.
+template <int DT, bool kVec>
+__device__ __forceinline__ int slot0(int c, int tid, int h) {
+  return c * FinGeom<DT, kVec>::CH + tid * FinGeom<DT, kVec>::E - h;
+}
+
+// Block `i` (16 bytes) of a row whose element 0 sits h elements into its block.
+template <int DT>
+__device__ __forceinline__ const uint4 *row_blocks(const void *row, int h) {
+  return reinterpret_cast<const uint4 *>(static_cast<const char *>(row) - h * Elt<DT>::kBytes);
+}
+
+// Weights of thread tid's slots of chunk c (0 outside [0, V)).
+template <int DT, bool kVec>
+__device__ __forceinline__ void thread_weights(const SampleJob &job, int V, int c, int tid, int h, float *w) {
   using E = Elt<DT>;
   using G = FinGeom<DT, kVec>;
-  const int k0 = c * G::CH + tid * G::E;
+  const int k0 = slot0<DT, kVec>(c, tid, h);
   const bool resid = job.mode == JOB_RESIDUAL;
-  if (kVec && k0 + G::E <= V) {
-    const int64_t vi = k0 / G::E;
-    const uint4 rt = load_vec(static_cast<const uint4 *>(job.t_row) + vi);
-    const uint4 rd = resid ? load_vec(static_cast<const uint4 *>(job.d_row) + vi) : make_uint4(0, 0, 0, 0);
+  if (kVec) {
+    if (k0 >= V) {
+#pragma unroll
+      for (int e = 0; e < G::E; ++e) w[e] = 0.0f;
+      return;
+    }
+    const int64_t blk = static_cast<int64_t>(c) * kFinThreads + tid;
+    const uint4 rt = load_vec(row_blocks<DT>(job.t_row, h) + blk);
+    const uint4 rd = resid ? load_vec(row_blocks<DT>(job.d_row, h) + blk) : make_uint4(0, 0, 0, 0);
     float xt[Elt<DT>::kEPV], xd[Elt<DT>::kEPV];
     E::vec(rt, xt);
     E::vec(rd, xd);
+    const bool whole = k0 >= 0 && k0 + G::E <= V;
 #pragma unroll
-    for (int e = 0; e < G::E; ++e) w[e] = weight_of(job, xt[e], xd[e]);
+    for (int e = 0; e < G::E; ++e) {
+      const float x = weight_of(job, xt[e], xd[e]);
+      w[e] = (whole || (k0 + e >= 0 && k0 + e < V)) ? x : 0.0f;
+    }
   } else {
 #pragma unroll
     for (int e = 0; e < G::E; ++e) {
@@ -629,10 +671,10 @@ __device__ __forceinline__ void thread_weights(const SampleJob &job, int V, int 
 
 // Sum of thread tid's weights of chunk c, then the wave sum into wp.
 template <int DT, bool kVec>
-__device__ __forceinline__ void chunk_sum_guarded(const SampleJob &job, int V, int c, float *wp, int tid) {
+__device__ __forceinline__ void chunk_sum_guarded(const SampleJob &job, int V, int c, int h, float *wp, int tid) {
   using G = FinGeom<DT, kVec>;
   float w[G::E];
-  thread_weights<DT, kVec>(job, V, c, tid, w);
+  thread_weights<DT, kVec>(job, V, c, tid, h, w);
   float t = 0.0f;
 #pragma unroll
   for (int e = 0; e < G::E; ++e) t += w[e];
@@ -660,20 +702,24 @@ __device__ __forceinline__ void batch_sums(const SampleJob &job, const uint4 *rt
 }
 
 // Streams chunks [c_begin, c_end) of the job's row(s) once;
-// wp[c * kFinWaves + wave] = wave sum of chunk c.  Aligned rows: chunks whose
-// vectors are all complete go in batches of kFinBatch, the next batch's loads
-// in flight while the current one is reduced; other chunks (the row's end) are
-// guarded per element.
+// wp[c * kFinWaves + wave] = wave sum of chunk c.  Vector geometry: chunks
+// whose slots all lie in [0, V) go in batches of kFinBatch, the next batch's
+// loads in flight while the current one is reduced; the head chunk (h > 0)
+// and the row's end are masked per slot.
 template <int DT, bool kVec>
-__device__ __forceinline__ void stream_chunk_sums(const SampleJob &job, int V, int c_begin, int c_end, float *wp,
-                                                  int tid) {
+__device__ __forceinline__ void stream_chunk_sums(const SampleJob &job, int V, int c_begin, int c_end, int h,
+                                                  float *wp, int tid) {
   int c = c_begin;
   if (kVec) {
-    constexpr int EPV = Elt<DT>::kEPV;
-    const int full = min(c_end, (V / EPV) / kFinThreads);  // chunks of complete vectors only
+    constexpr int CH = FinGeom<DT, true>::CH;
+    if (h > 0 && c == 0 && c < c_end) {
+      chunk_sum_guarded<DT, true>(job, V, 0, h, wp, tid);
+      c = 1;
+    }
+    const int full = min(c_end, (V + h) / CH);  // chunks with every slot inside the row
     const bool resid = job.mode == JOB_RESIDUAL;
-    const uint4 *tv = reinterpret_cast<const uint4 *>(job.t_row) + tid;
-    const uint4 *dv = reinterpret_cast<const uint4 *>(job.d_row) + tid;
+    const uint4 *tv = row_blocks<DT>(job.t_row, h) + tid;
+    const uint4 *dv = row_blocks<DT>(job.d_row, h) + tid;
     const uint4 zero = make_uint4(0, 0, 0, 0);
     if (full - c >= kFinBatch) {
       uint4 at[kFinBatch], ad[kFinBatch], bt[kFinBatch], bd[kFinBatch];
@@ -699,7 +745,7 @@ __device__ __forceinline__ void stream_chunk_sums(const SampleJob &job, int V, i
       c += kFinBatch;
     }
   }
-  for (; c < c_end; ++c) chunk_sum_guarded<DT, kVec>(job, V, c, wp, tid);
+  for (; c < c_end; ++c) chunk_sum_guarded<DT, kVec>(job, V, c, h, wp, tid);
 }
 
 // cs[c] = sum over waves of wp[c][wave], in wave order, for c in [c_begin, c_end).
@@ -717,7 +763,7 @@ __device__ __forceinline__ void chunk_totals(const float *wp, int c_begin, int c
 // running sum exceeds tau (w_k > 0); if rounding leaves none, the chunk's last
 // k with w_k > 0.  cs must be visible to the whole workgroup.
 template <int DT, bool kVec>
-__device__ int draw_from_sums(const SampleJob &job, int V, int C, const float *cs, int tid) {
+__device__ int draw_from_sums(const SampleJob &job, int V, int C, int h, const float *cs, int tid) {
   using G = FinGeom<DT, kVec>;
   __shared__ float s_base, s_tau;
   __shared__ int s_chunk, s_cand, s_last;
@@ -757,7 +803,7 @@ __device__ int draw_from_sums(const SampleJob &job, int V, int C, const float *c
   __syncthreads();
   const int chunk = s_chunk;
   float w[G::E];
-  thread_weights<DT, kVec>(job, V, chunk, tid, w);
+  thread_weights<DT, kVec>(job, V, chunk, tid, h, w);
   float ts = 0.0f;
 #pragma unroll
   for (int e = 0; e < G::E; ++e) ts += w[e];
@@ -776,7 +822,7 @@ __device__ int draw_from_sums(const SampleJob &job, int V, int C, const float *c
   for (int k = 0; k < wave; ++k) wave_off += s_wave_tot[k];
   float run = s_base + (wave_off + excl);
   const float tau = s_tau;
-  const int k0 = chunk * G::CH + tid * G::E;
+  const int k0 = slot0<DT, kVec>(chunk, tid, h);
   int cand = INT_MAX, last = -1;
 #pragma unroll
   for (int e = 0; e < G::E; ++e) {
@@ -788,13 +834,29 @@ __device__ int draw_from_sums(const SampleJob &job, int V, int C, const float *c
   if (last >= 0) atomicMax(&s_last, last);
   __syncthreads();
   int y = s_cand != INT_MAX ? s_cand : s_last;
-  if (y < 0) y = chunk * G::CH;  // no mass anywhere: only reachable with invalid logits
+  if (y < 0) y = max(0, chunk * G::CH - h);  // no mass anywhere: only reachable with invalid logits
   return y;
 }
 
-template <int DT, bool kVec>
-__device__ __forceinline__ int finish_chunks(int V) {
-  return (V + FinGeom<DT, kVec>::CH - 1) / FinGeom<DT, kVec>::CH;
+// Sampling pass of one job over chunks [0, C) and the draw, by the whole
+// workgroup; chunk sums in s_cs.
+template <int DT>
+__device__ __forceinline__ int sample_job(const SampleJob &job, int V, float *s_wp, float *s_cs, int tid) {
+  const int h = job_shift(job, Elt<DT>::kBytes);
+  if (h >= 0) {
+    const int C = finish_chunks<DT, true>(V, h);
+    stream_chunk_sums<DT, true>(job, V, 0, C, h, s_wp, tid);
+    __syncthreads();
+    chunk_totals(s_wp, 0, C, s_cs, tid);
+    __syncthreads();
+    return draw_from_sums<DT, true>(job, V, C, h, s_cs, tid);
+  }
+  const int C = finish_chunks<DT, false>(V, 0);
+  stream_chunk_sums<DT, false>(job, V, 0, C, 0, s_wp, tid);
+  __syncthreads();
+  chunk_totals(s_wp, 0, C, s_cs, tid);
+  __syncthreads();
+  return draw_from_sums<DT, false>(job, V, C, 0, s_cs, tid);
 }
 
 // Job of sequence b into s_job: decided here (window, wave 0; writes the
@@ -822,22 +884,7 @@ __global__ void __launch_bounds__(kFinThreads) k_finish(WindowArgs A, const Samp
   load_job<DT, kWindow>(A, jobs, b, true, &s_job, tid);
   const SampleJob job = s_job;
   if (job.mode == JOB_NONE) return;
-  int y;
-  if (job_rows_aligned(job)) {
-    const int C = finish_chunks<DT, true>(V);
-    stream_chunk_sums<DT, true>(job, V, 0, C, s_wp, tid);
-    __syncthreads();
-    chunk_totals(s_wp, 0, C, s_cs, tid);
-    __syncthreads();
-    y = draw_from_sums<DT, true>(job, V, C, s_cs, tid);
-  } else {
-    const int C = finish_chunks<DT, false>(V);
-    stream_chunk_sums<DT, false>(job, V, 0, C, s_wp, tid);
-    __syncthreads();
-    chunk_totals(s_wp, 0, C, s_cs, tid);
-    __syncthreads();
-    y = draw_from_sums<DT, false>(job, V, C, s_cs, tid);
-  }
+  const int y = sample_job<DT>(job, V, s_wp, s_cs, tid);
   if (tid == 0) *job.out_slot = y;
 }
 
@@ -858,12 +905,13 @@ __global__ void __launch_bounds__(kFinThreads) k_finish_part(WindowArgs A, Sampl
   const SampleJob job = s_job;
   if (kWindow && g == 0 && tid == 0) jobs[b] = job;
   if (job.mode == JOB_NONE) return;
-  const bool vec = job_rows_aligned(job);
-  const int C = vec ? finish_chunks<DT, true>(V) : finish_chunks<DT, false>(V);
+  const int h = job_shift(job, Elt<DT>::kBytes);
+  const bool vec = h >= 0;
+  const int C = vec ? finish_chunks<DT, true>(V, h) : finish_chunks<DT, false>(V, 0);
   const int c0 = static_cast<int>(static_cast<int64_t>(C) * g / G);
   const int c1 = static_cast<int>(static_cast<int64_t>(C) * (g + 1) / G);
-  if (vec) stream_chunk_sums<DT, true>(job, V, c0, c1, s_wp, tid);
-  else stream_chunk_sums<DT, false>(job, V, c0, c1, s_wp, tid);
+  if (vec) stream_chunk_sums<DT, true>(job, V, c0, c1, h, s_wp, tid);
+  else stream_chunk_sums<DT, false>(job, V, c0, c1, 0, s_wp, tid);
   __syncthreads();
   chunk_totals(s_wp, c0, c1, s_cs, tid);
   __syncthreads();
@@ -879,12 +927,194 @@ __global__ void __launch_bounds__(kFinThreads) k_finish_select(const SampleJob *
   __shared__ float s_cs[kFinMaxChunks];
   const SampleJob job = jobs[b];
   if (job.mode == JOB_NONE) return;
-  const bool vec = job_rows_aligned(job);
-  const int C = vec ? finish_chunks<DT, true>(V) : finish_chunks<DT, false>(V);
+  const int h = job_shift(job, Elt<DT>::kBytes);
+  const bool vec = h >= 0;
+  const int C = vec ? finish_chunks<DT, true>(V, h) : finish_chunks<DT, false>(V, 0);
   for (int c = tid; c < C; c += kFinThreads) s_cs[c] = spart[static_cast<int64_t>(b) * cmax + c];
   __syncthreads();
-  const int y = vec ? draw_from_sums<DT, true>(job, V, C, s_cs, tid) : draw_from_sums<DT, false>(job, V, C, s_cs, tid);
+  const int y = vec ? draw_from_sums<DT, true>(job, V, C, h, s_cs, tid)
+                    : draw_from_sums<DT, false>(job, V, C, 0, s_cs, tid);
   if (tid == 0) *job.out_slot = y;
+}
+
+// ---------------------------------------------------------------------------
+// Token tree, lossless multi-candidate walk (one 1024-thread workgroup per
+// sequence)
+// ---------------------------------------------------------------------------
+// SpecInfer's multi-round scheme (cited by title on the PipeSpec and CLaSp
+// review pages): from the root, the children of the current node w are tried
+// in index order against the residual r of w.  After j rejections at w,
+// r = max(0, p - c q) / Z with c = 0, Z = 1 at first and, per rejection,
+// c <- c + Z, Z <- sum_k max(0, p_k - c q_k) (p, q: rows w of the target and
+// draft).  This closed form equals renormalising max(0, r - q) after every
+// rejection.  Child token x is accepted iff u * q(x) * Z < p(x) - c q(x),
+// which with c = 0, Z = 1 is the window's u * q < p.  An accepted child
+// becomes w and r restarts at its p.  A leaf ends the walk with a bonus draw
+// from p_w; a node whose children were all rejected ends it with a draw from
+// r, using the chunk sums of the pass that produced Z.  A rejection whose new
+// residual has no mass (r equal to q) keeps the previous r.
+//
+// Set-up, one thread per node v: p_w(x_v), q_w(x_v) and u_v against the
+// parent w, the exponent offsets of rows v, the draw uniform after v, and the
+// child links, all into LDS.  Then thread 0 walks through LDS alone; every
+// thread joins the streaming passes (one per rejection, over rows w of both
+// logits) and the final draw.
+enum : int { WALK_PASS = 0, WALK_PASS_DRAW = 1, WALK_DRAW = 2 };
+
+template <int DT>
+__global__ void __launch_bounds__(kFinThreads) k_tree_walk(TreeArgs A) {
+  using E = Elt<DT>;
+  static_assert(kFinThreads >= kTreeMaxNodes, "one thread per node in the set-up");
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int N = A.meta.N;
+  const int D = A.meta.max_depth;
+  const int V = A.V;
+  int32_t *out_t = A.out_tokens + static_cast<int64_t>(b) * (D + 1);
+  int32_t *out_n = A.out_nodes + static_cast<int64_t>(b) * D;
+  const int32_t *toks = A.tokens + static_cast<int64_t>(b) * N;
+  const int tok = (tid >= 1 && tid < N) ? toks[tid] : 0;
+  const bool bad = tid >= 1 && tid < N && (tok < 0 || tok >= V);
+  if (__syncthreads_or(bad)) {
+    for (int k = tid; k <= D; k += kFinThreads) out_t[k] = -1;
+    for (int k = tid; k < D; k += kFinThreads) out_n[k] = -1;
+    if (tid == 0) {
+      A.n_accepted[b] = -1;
+      A.best_node[b] = -1;
+    }
+    return;
+  }
+  const float2 *prow = A.part + static_cast<int64_t>(b) * A.R * A.S;
+  const int64_t row_bytes = static_cast<int64_t>(V) * E::kBytes;
+  const char *t0 = A.t + b * A.seq_bytes;
+  const char *d0 = A.d + b * A.seq_bytes;
+  const uint64_t seq = A.seq_ids ? A.seq_ids[b] : static_cast<uint64_t>(b);
+  const int64_t base = A.base_pos ? A.base_pos[b] : 0;
+
+  __shared__ SampleJob s_job;
+  __shared__ float s_wp[kFinMaxChunks * kFinWaves];
+  __shared__ float s_cs[kFinMaxChunks];
+  __shared__ float s_P[kTreeMaxNodes], s_Q[kTreeMaxNodes], s_u[kTreeMaxNodes];
+  __shared__ float s_ct[kTreeMaxNodes], s_cd[kTreeMaxNodes], s_v[kTreeMaxNodes];
+  __shared__ int s_first[kTreeMaxNodes], s_next[kTreeMaxNodes], s_tok[kTreeMaxNodes];
+  __shared__ int s_path[kTreeMaxDepth];
+  __shared__ int s_cmd, s_nd, s_w;
+
+  if (tid < N) {
+    const int v = tid;
+    const int first = A.meta.first_child[v];
+    const int depth = A.meta.depth[v];
+    const int rank = A.meta.rank[v];
+    s_ct[v] = norm_offset(row_maxsum(prow + v * A.S, A.S));
+    s_cd[v] = first >= 0 ? norm_offset(row_maxsum(prow + (N + v) * A.S, A.S)) : 0.0f;
+    s_v[v] = uniform24(
+        philox4x64_10({seq, static_cast<uint64_t>(base + depth + 1), static_cast<uint64_t>(rank), 0}, A.seed, A.tag)
+            .c1);
+    if (v >= 1) {
+      const int w = A.meta.parent[v];
+      const MaxSum st = row_maxsum(prow + w * A.S, A.S);
+      const MaxSum sd = row_maxsum(prow + (N + w) * A.S, A.S);
+      s_P[v] = prob_at(E::one(t0 + w * row_bytes, tok), st);
+      s_Q[v] = prob_at(E::one(d0 + w * row_bytes, tok), sd);
+      s_u[v] = uniform24(
+          philox4x64_10({seq, static_cast<uint64_t>(base + depth), static_cast<uint64_t>(rank), 0}, A.seed, A.tag)
+              .c0);
+    }
+    s_first[v] = first;
+    s_next[v] = A.meta.next_sibling[v];
+    s_tok[v] = tok;
+  }
+  __syncthreads();
+
+  // walk state, meaningful in thread 0 only
+  int w = 0, nd = 0, cand = s_first[0], pend_chunks = 0;
+  float c = 0.0f, Z = 1.0f, c_try = 0.0f;
+  bool pending = false, sums_ok = false;
+  for (;;) {
+    if (tid == 0) {
+      if (pending) {  // s_cs holds the chunk sums of max(0, p - c_try q)
+        float z = 0.0f;
+        for (int k = 0; k < pend_chunks; ++k) z += s_cs[k];
+        sums_ok = z > 0.0f;
+        if (sums_ok) {
+          c = c_try;
+          Z = z;
+        }
+        pending = false;
+      }
+      SampleJob jb{};
+      int cmd = -1;
+      while (cmd < 0) {
+        jb.t_row = t0 + w * row_bytes;
+        jb.ct = s_ct[w];
+        if (cand >= 0) {
+          const float P = s_P[cand], Q = s_Q[cand];
+          if (s_u[cand] * Q * Z < __builtin_fmaf(-c, Q, P)) {
+            s_path[nd++] = cand;
+            w = cand;
+            cand = s_first[w];
+            c = 0.0f;
+            Z = 1.0f;
+            sums_ok = false;
+            continue;
+          }
+          c_try = c + Z;
+          jb.mode = JOB_RESIDUAL;
+          jb.d_row = d0 + w * row_bytes;
+          jb.cd = s_cd[w];
+          jb.cq = c_try;
+          pending = true;
+          cand = s_next[cand];
+          cmd = WALK_PASS;
+        } else {
+          if (s_first[w] >= 0 && c > 0.0f) {
+            jb.mode = JOB_RESIDUAL;
+            jb.d_row = d0 + w * row_bytes;
+            jb.cd = s_cd[w];
+            jb.cq = c;
+          } else {  // a leaf, or no rejection left residual mass: draw from p
+            jb.mode = JOB_BONUS;
+            jb.d_row = nullptr;
+            jb.cd = 0.0f;
+            jb.cq = 0.0f;
+          }
+          jb.v = s_v[w];
+          jb.out_slot = out_t + nd;
+          cmd = (jb.mode == JOB_RESIDUAL && sums_ok) ? WALK_DRAW : WALK_PASS_DRAW;
+        }
+      }
+      const int hj = job_shift(jb, E::kBytes);
+      pend_chunks = hj >= 0 ? finish_chunks<DT, true>(V, hj) : finish_chunks<DT, false>(V, 0);
+      s_job = jb;
+      s_cmd = cmd;
+      s_nd = nd;
+      s_w = w;
+    }
+    __syncthreads();
+    const SampleJob job = s_job;
+    const int cmd = s_cmd;
+    const int h = job_shift(job, E::kBytes);
+    const bool vec = h >= 0;
+    const int C = vec ? finish_chunks<DT, true>(V, h) : finish_chunks<DT, false>(V, 0);
+    if (cmd != WALK_DRAW) {
+      if (vec) stream_chunk_sums<DT, true>(job, V, 0, C, h, s_wp, tid);
+      else stream_chunk_sums<DT, false>(job, V, 0, C, 0, s_wp, tid);
+      __syncthreads();
+      chunk_totals(s_wp, 0, C, s_cs, tid);
+      __syncthreads();
+    }
+    if (cmd == WALK_PASS) continue;
+    const int y = vec ? draw_from_sums<DT, true>(job, V, C, h, s_cs, tid)
+                      : draw_from_sums<DT, false>(job, V, C, 0, s_cs, tid);
+    const int n = s_nd;
+    for (int k = tid; k < D; k += kFinThreads) out_n[k] = k < n ? s_path[k] : -1;
+    for (int k = tid; k <= D; k += kFinThreads) out_t[k] = k < n ? s_tok[s_path[k]] : (k == n ? y : -1);
+    if (tid == 0) {
+      A.n_accepted[b] = n;
+      A.best_node[b] = s_w;
+    }
+    return;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1033,6 +1263,14 @@ void launch_tree_decide(int dtype, const TreeArgs &A, int B, hipStream_t st) {
 void launch_tree_finish(int dtype, SampleJob *jobs, int B, int V, float *spart, int cmax, hipStream_t st) {
   const WindowArgs none{};
   launch_finish<false>(dtype, none, jobs, B, V, spart, cmax, st);
+}
+
+void launch_tree_walk(int dtype, const TreeArgs &A, int B, hipStream_t st) {
+  switch (dtype) {
+    case DT_BF16: hipLaunchKernelGGL(k_tree_walk<DT_BF16>, dim3(B), dim3(kFinThreads), 0, st, A); break;
+    case DT_F16: hipLaunchKernelGGL(k_tree_walk<DT_F16>, dim3(B), dim3(kFinThreads), 0, st, A); break;
+    default: hipLaunchKernelGGL(k_tree_walk<DT_F32>, dim3(B), dim3(kFinThreads), 0, st, A); break;
+  }
 }
 
 void launch_rollback(const RollbackArgs &A, int S, int stage, hipStream_t st) {

@@ -93,6 +93,7 @@ void launch_stage_decide(int dtype, const WindowArgs &A, int B, int lo, int hi, 
 void launch_greedy_decide(const GreedyArgs &A, int B, hipStream_t st);
 void launch_tree_decide(int dtype, const TreeArgs &A, int B, hipStream_t st);
 void launch_tree_finish(int dtype, SampleJob *jobs, int B, int V, float *spart, int cmax, hipStream_t st);
+void launch_tree_walk(int dtype, const TreeArgs &A, int B, hipStream_t st);
 void launch_rollback(const RollbackArgs &A, int S, int stage, hipStream_t st);
 int probe_blocks(size_t bytes);
 void launch_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t st);

@@ -17,7 +17,10 @@ constexpr int kFinThreads = SV_FIN_THREADS;  // sampling workgroup (one per sequ
 constexpr int kFinWaves = kFinThreads / 64;
 constexpr int kFinBatch = SV_FIN_BATCH;      // chunks per pipelined batch
 constexpr int kMaxVocab = 1 << 21;    // 2,097,152 tokens
-constexpr int kFinMaxChunks = kMaxVocab / (kFinThreads * 4);  // 512 at 1024 threads
+// Chunks of a sampling pass: at most ceil((V + 3) / (4 kFinThreads)) (four
+// slots per thread and up to 3 slots of head offset); 513 at 1024 threads.
+constexpr int fin_chunks_max(int V) { return (V + 3 + kFinThreads * 4 - 1) / (kFinThreads * 4); }
+constexpr int kFinMaxChunks = fin_chunks_max(kMaxVocab);
 constexpr int kFinFillWorkgroups = 256;  // draw workgroups wanted per launch
 constexpr int kMaxSegments = 64;      // row segments (split-row mode)
 constexpr int64_t kFillWorkgroups = 16384;  // row workgroups per launch (256 CUs)
@@ -25,7 +28,9 @@ constexpr int kMinSegment = 4096;     // elements; below this a split does not p
 
 // Work item of the sampling pass of one sequence: draw from
 //   w_k = p_k                       (BONUS)
-//   w_k = max(0, p_k - q_k)         (RESIDUAL)
+//   w_k = max(0, p_k - cq * q_k)    (RESIDUAL; cq = 1 for a window or a node's
+//                                    first residual, larger after several
+//                                    rejected siblings)
 // with p_k = 2^(t_k log2e - ct), q_k = 2^(d_k log2e - cd); the offsets carry
 // the row maximum and the log of the row's normaliser.
 enum : int { JOB_NONE = 0, JOB_BONUS = 1, JOB_RESIDUAL = 2 };
@@ -37,7 +42,8 @@ struct SampleJob {
   float ct, cd;
   float v;            // sampling uniform
   int32_t mode;
-  int32_t pad[6];
+  float cq;           // coefficient of q in the residual (>= 1)
+  int32_t pad[5];
 };
 static_assert(sizeof(SampleJob) == 64, "SampleJob is one 64-byte record");
 
@@ -50,8 +56,11 @@ struct TreeMeta {
   uint64_t internal[kTreeMaxNodes / 64];  // bit v: node v has children
   int16_t parent[kTreeMaxNodes];
   int16_t rank[kTreeMaxNodes];
+  int16_t first_child[kTreeMaxNodes];     // smallest child index, or -1
+  int16_t next_sibling[kTreeMaxNodes];    // next larger index with the same parent, or -1
   uint8_t depth[kTreeMaxNodes];
 };
+static_assert(sizeof(TreeMeta) <= 2560, "tree metadata travels in the kernel arguments");
 
 struct RowPlan {
   int S;        // segments per row
@@ -93,7 +102,7 @@ inline Layout make_layout(int op, int64_t B, int32_t n, int32_t V) {
   off = align256(off + sizeof(float) * 2 * static_cast<size_t>(B) * L.rows_per_seq * L.plan.S);
   L.jobs_off = off;
   off = align256(off + (op == 1 ? 0 : sizeof(SampleJob) * static_cast<size_t>(B)));
-  L.cmax = (op == 1) ? 0 : (V + kFinThreads * 4 - 1) / (kFinThreads * 4);
+  L.cmax = (op == 1) ? 0 : fin_chunks_max(V);
   L.spart_off = off;
   off = align256(off + sizeof(float) * static_cast<size_t>(B) * L.cmax);
   L.status_off = off;  // early-exit window: per-sequence status

@@ -70,7 +70,7 @@ typedef enum {
 
 typedef enum { SV_OP_WINDOW = 0, SV_OP_GREEDY = 1, SV_OP_TREE = 2 } sv_op;
 
-typedef enum { SV_TREE_GREEDY = 0, SV_TREE_STOCHASTIC = 1 } sv_tree_mode;
+typedef enum { SV_TREE_GREEDY = 0, SV_TREE_STOCHASTIC = 1, SV_TREE_MULTI_CANDIDATE = 2 } sv_tree_mode;
 
 #define SV_MAX_GAMMA 64
 #define SV_TREE_MAX_NODES 256
@@ -174,15 +174,30 @@ int32_t sv_tree_max_depth(const int32_t *parent_host, int32_t N);
  *   parent_host   HOST [N]: parent[0] = -1, 0 <= parent[v] < v (BFS or any
  *                 topological order); N <= SV_TREE_MAX_NODES, depth <=
  *                 SV_TREE_MAX_DEPTH; read during the call only.
- *   mode: SV_TREE_GREEDY or SV_TREE_STOCHASTIC.
- * Node v >= 1 is accepted when its parent is accepted and its token passes the
- * test against the parent's row (argmax equality, or u_v q_w < p_w).  The
- * deepest accepted node d (smallest index among equals) ends the path.
+ *   mode: SV_TREE_GREEDY, SV_TREE_STOCHASTIC or SV_TREE_MULTI_CANDIDATE.
+ * GREEDY / STOCHASTIC: node v >= 1 is accepted when its parent is accepted
+ * and its token passes the test against the parent's row (argmax equality, or
+ * u_v q_w < p_w).  The deepest accepted node d (smallest index among equals)
+ * ends the path.  With more than one child per node the STOCHASTIC rule does
+ * not keep the target distribution.
+ * MULTI_CANDIDATE: the multi-round scheme of SpecInfer (cited by title on the
+ * PipeSpec and CLaSp review pages), which keeps the target distribution when
+ * siblings are i.i.d. draws from their parent's draft row.  From the root,
+ * the children of the current node w are tried in index order against a
+ * residual r that starts at p_w: child v (token x) is accepted when
+ * u_v q_w(x) < r(x); after a rejection r becomes the renormalised
+ * max(0, r - q_w) (kept as it is if that has no mass).  An accepted child
+ * becomes w; the walk ends at a leaf (bonus draw from p_w) or at a node whose
+ * children were all rejected (draw from r).  d is the final node.  One
+ * 1024-thread workgroup per sequence makes one pass over rows w of both
+ * logits per rejection.
+ * Uniforms: node v's test uses word 0 at (base_pos + depth(v), rank(v)); the
+ * token drawn after d uses word 1 at (base_pos + depth(d) + 1, rank(d)).
  * Outputs (D = sv_tree_max_depth):
  *   n_accepted [B] = depth(d) (or -1); best_node [B] = d;
  *   out_tokens [B][D+1]: path tokens, then argmax(row d) (greedy), a bonus
- *              draw from p_d (d a leaf) or a draw from the renormalised
- *              max(0, p_d - q_d), then -1;
+ *              draw from p_d (d a leaf) or a draw from the residual at d,
+ *              then -1;
  *   out_nodes  [B][D]: path node ids, then -1. */
 int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtype,
                    const int32_t *node_tokens, const int32_t *parent_host,

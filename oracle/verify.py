@@ -374,6 +374,8 @@ def verify_tree_multiround(target, draft, node_tokens, parent, u_node, v_node):
     sample["kind"] = kind
     sample["y"] = int(y)
     sample["weights"] = r
+    sample["mass"] = mass
+    sample["shift"] = shift
     return {
         "n": depth[w],
         "best": w,

@@ -134,3 +134,67 @@ def check_tree(data, res, mode, *, seed=0, tag=0, rows=None):
             assert depth_margin, (b, int(best_gpu[b]), o["best"])
         margins += 1
     return len(rows), margins
+
+
+def _walk_decision_margin(tests):
+    """A sibling test decided within the margin: |u - r(x)/q(x)| scaled by the
+    condition of the float32 closed form (p(x) + shift q(x)) / (q(x) mass)."""
+    for t in tests:
+        if t["q"] <= 0.0 or not np.isfinite(t["ratio"]):
+            continue
+        cond = (t["p"] + t["shift"] * t["q"]) / (t["q"] * t["mass"])
+        if abs(t["u"] - t["ratio"]) < MARGIN * max(1.0, cond):
+            return True
+    return False
+
+
+def _walk_sample_margin(s):
+    """The draw within the margin; residual weights after several rejections
+    carry float32 error ~(1 + shift) relative to the total mass."""
+    if s is None:
+        return False
+    Z = s["Z"]
+    tol = MARGIN * (1.0 + s["shift"]) / s["mass"]
+    return abs(s["tau"] - s["C_lo"]) / Z < tol or abs(s["tau"] - s["C_hi"]) / Z < tol
+
+
+def check_tree_walk(data, res, *, seed=0, tag=0, seq_ids=None, base_pos=None, rows=None):
+    """Compares sv_verify_tree(MULTI_CANDIDATE) with oracle.verify_tree_multiround.
+    Returns (n_checked, n_margin_cases, n_rejected_tests)."""
+    dtype = data["dtype"]
+    parent = data["parent"]
+    B, N = data["tokens"].shape
+    depth, rank, _ = oracle.tree_meta(parent)
+    D = max(depth)
+    rows = range(B) if rows is None else rows
+    toks = data["tokens"].cpu().numpy()
+    n_gpu = res.n_accepted.cpu().numpy()
+    best_gpu = res.best_node.cpu().numpy()
+    out_gpu = res.out_tokens.cpu().numpy()
+    nodes_gpu = res.out_nodes.cpu().numpy()
+    sid = seq_ids.cpu().numpy() if seq_ids is not None else None
+    bp = base_pos.cpu().numpy() if base_pos is not None else None
+    margins = 0
+    rejected = 0
+    for b in rows:
+        T = host_rows(data["target"][b], dtype)
+        Dl = host_rows(data["draft"][b], dtype)
+        s = int(sid[b]) if sid is not None else b
+        base = int(bp[b]) if bp is not None else 0
+        un, vn = oracle.tree_uniforms(seed, tag, s, base, depth, rank)
+        o = oracle.verify_tree_multiround(T, Dl, toks[b], parent, un, vn)
+        rejected += sum(1 for t in o["tests"] if t["node"] not in o["path"])
+        want_t = o["out"] + [-1] * (D + 1 - len(o["out"]))
+        want_n = o["path"] + [-1] * (D - len(o["path"]))
+        same = (int(n_gpu[b]) == o["n"] and int(best_gpu[b]) == o["best"]
+                and list(out_gpu[b]) == want_t and list(nodes_gpu[b]) == want_n)
+        if same:
+            continue
+        if int(best_gpu[b]) == o["best"] and list(nodes_gpu[b]) == want_n:
+            assert list(out_gpu[b][:o["n"]]) == o["out"][:o["n"]]
+            assert _walk_sample_margin(o["sample"]) or _walk_decision_margin(o["tests"]), \
+                (b, list(out_gpu[b]), want_t, o["sample"])
+        else:
+            assert _walk_decision_margin(o["tests"]), (b, list(nodes_gpu[b]), want_n)
+        margins += 1
+    return len(rows), margins, rejected

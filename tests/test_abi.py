@@ -98,6 +98,11 @@ def test_bad_host_arguments_return_status_without_device_work():
                             fake, fake, fake, fake, fake, 1 << 20, None) == -1
     assert L.sv_verify_tree(fake, None, 1, fake, par, 1, 3, 100, 1, 0, 0, None, None,
                             fake, fake, fake, fake, fake, 1 << 20, None) == -1
+    # multi-candidate walk without draft logits
+    assert L.sv_verify_tree(fake, None, 1, fake, par, 1, 3, 100, 2, 0, 0, None, None,
+                            fake, fake, fake, fake, fake, 1 << 20, None) == -1
+    assert L.sv_verify_tree(fake, fake, 1, fake, par, 1, 3, 100, 3, 0, 0, None, None,
+                            fake, fake, fake, fake, fake, 1 << 20, None) == -1
     # rollback: stage outside [1, K-1], null buffers
     assert L.sv_rollback(fake, fake, 4, 3, 8, 3, fake, 8, fake, 0, None) == -1
     assert L.sv_rollback(fake, fake, 4, 3, 8, 0, fake, 8, fake, 0, None) == -1
