@@ -37,6 +37,8 @@ from .verify import (
     tree_meta,
     verify_tree,
     verify_tree_multiround,
+    lmhead_logits,
+    verify_window_lmhead,
     rollback,
     hierarchy_three_stage,
 )
@@ -55,6 +57,8 @@ __all__ = [
     "tree_meta",
     "verify_tree",
     "verify_tree_multiround",
+    "lmhead_logits",
+    "verify_window_lmhead",
     "rollback",
     "hierarchy_three_stage",
 ]

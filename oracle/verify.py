@@ -39,6 +39,8 @@ Pins: tests/test_oracle_*.py (brute-force exact laws at V=8, chi-square on
 Philox-driven windows, the pages' expected-length and steady-state formulas on
 exact-alpha inputs, scipy softmax/logsumexp, numpy argmax, special cases,
 chain tree == window, brute-force tree paths, rollback invariants; for the
+LM-head logits: one-hot unembeddings reduce it to the window on the hidden
+values, and it is invariant under exact rescaling and vocabulary permutation;
 multi-candidate walk: its exact output law equals the target's autoregressive
 law on enumerated small trees, chain == window, and the closed form of the
 residual after j rejections).
@@ -384,6 +386,28 @@ def verify_tree_multiround(target, draft, node_tokens, parent, u_node, v_node):
         "tests": tests,
         "sample": sample,
     }
+
+
+# --------------------------------------------------------------------------
+# logits from hidden states (LM head) feeding the window
+# --------------------------------------------------------------------------
+
+
+def lmhead_logits(hidden, unembed):
+    """Logits of each row of `hidden` (rows, H) against the unembedding
+    `unembed` (V, H): logits[r, k] = sum_h hidden[r, h] * unembed[k, h], in
+    float64 (products of bf16 values are exact in float64)."""
+    hidden = np.asarray(hidden, dtype=np.float64)
+    unembed = np.asarray(unembed, dtype=np.float64)
+    return hidden @ unembed.T
+
+
+def verify_window_lmhead(h_target, w_target, h_draft, w_draft, tokens, length, u, v):
+    """The speculative-sampling window on logits produced from hidden states:
+    target rows h_target (gamma+1, Ht) x w_target (V, Ht), draft rows
+    h_draft (gamma, Hd) x w_draft (V, Hd); then verify_window."""
+    return verify_window(lmhead_logits(h_target, w_target), lmhead_logits(h_draft, w_draft),
+                         tokens, length, u, v)
 
 
 # --------------------------------------------------------------------------
