@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     workspace_size,
     workspace,
     verify_window,
+    verify_window_lmhead,
     verify_greedy,
     verify_tree,
     tree_max_depth,
@@ -20,10 +21,11 @@ from .api import (  # noqa: F401
     SV_OP_WINDOW,
     SV_OP_GREEDY,
     SV_OP_TREE,
+    SV_OP_LMHEAD,
 )
 
 __all__ = [
     "SvError", "WindowResult", "TreeResult", "workspace_size", "workspace",
-    "verify_window", "verify_greedy", "verify_tree", "tree_max_depth", "rollback",
+    "verify_window", "verify_window_lmhead", "verify_greedy", "verify_tree", "tree_max_depth", "rollback",
     "probe_read",
 ]

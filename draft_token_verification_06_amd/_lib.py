@@ -28,6 +28,8 @@ _SIGNATURES = {
     "sv_verify_tree": (_c.c_int, [_P, _P, _c.c_int, _P, _P, _I32, _I32, _I32, _c.c_int,
                                   _U64, _U64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "sv_rollback": (_c.c_int, [_P, _P, _I32, _I32, _I32, _I32, _P, _I64, _P, _I32, _P]),
+    "sv_verify_window_lmhead": (_c.c_int, [_P, _P, _I32, _P, _P, _I32, _P, _P, _I32, _I32, _I32,
+                                           _U64, _U64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "sv_probe_blocks": (_I32, [_SZ]),
     "sv_probe_read": (_c.c_int, [_P, _SZ, _P, _P]),
 }

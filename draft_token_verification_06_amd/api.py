@@ -12,7 +12,7 @@ import torch
 
 from ._lib import lib
 
-SV_OP_WINDOW, SV_OP_GREEDY, SV_OP_TREE = 0, 1, 2
+SV_OP_WINDOW, SV_OP_GREEDY, SV_OP_TREE, SV_OP_LMHEAD = 0, 1, 2, 3
 SV_TREE_GREEDY, SV_TREE_STOCHASTIC, SV_TREE_MULTI_CANDIDATE = 0, 1, 2
 _TREE_MODES = {"greedy": SV_TREE_GREEDY, "stochastic": SV_TREE_STOCHASTIC,
                "multi_candidate": SV_TREE_MULTI_CANDIDATE}
@@ -127,6 +127,43 @@ def verify_window(target, draft, tokens, *, seed=0, tag=0, window_len=None, seq_
     with torch.cuda.device(dev):
         _check(head[0](
             *head[1:], _ptr(target), ts, _ptr(draft), ds, _DTYPE_CODE[target.dtype],
+            _ptr(tokens), _ptr(window_len), B, gamma, V,
+            ctypes.c_uint64(seed), ctypes.c_uint64(tag), _ptr(seq_ids), _ptr(base_pos),
+            _ptr(out.n_accepted), _ptr(out.out_tokens), _ptr(out.p_draft), _ptr(out.q_draft),
+            _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def verify_window_lmhead(h_target, w_target, h_draft, w_draft, tokens, *, seed=0, tag=0,
+                         window_len=None, seq_ids=None, base_pos=None, return_probs=False, ws=None):
+    """Window verification on logits from hidden states, LM head fused:
+    sv_verify_window_lmhead.  h_target (B, gamma+1, Ht), w_target (V, Ht),
+    h_draft (B, gamma, Hd), w_draft (V, Hd), all bf16 and contiguous."""
+    B, rows, Ht = h_target.shape
+    gamma = rows - 1
+    V = w_target.shape[0]
+    for name, t in (("h_target", h_target), ("w_target", w_target), ("h_draft", h_draft),
+                    ("w_draft", w_draft)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous bf16 device tensor")
+    Hd = h_draft.shape[2]
+    if h_draft.shape[:2] != (B, gamma) or w_target.shape != (V, Ht) or w_draft.shape != (V, Hd):
+        raise ValueError("hidden / unembedding shapes do not agree")
+    _i32(tokens, (B, gamma), "tokens")
+    _optional(window_len, torch.int32, B, "window_len")
+    _optional(seq_ids, torch.int64, B, "seq_ids")
+    _optional(base_pos, torch.int64, B, "base_pos")
+    dev = h_target.device
+    if ws is None:
+        ws = workspace(SV_OP_LMHEAD, B, gamma, V, torch.bfloat16, dev)
+    out = WindowResult(torch.empty(B, dtype=torch.int32, device=dev),
+                       torch.empty(B, gamma + 1, dtype=torch.int32, device=dev))
+    if return_probs:
+        out.p_draft = torch.empty(B, gamma, dtype=torch.float32, device=dev)
+        out.q_draft = torch.empty(B, gamma, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().sv_verify_window_lmhead(
+            _ptr(h_target), _ptr(w_target), Ht, _ptr(h_draft), _ptr(w_draft), Hd,
             _ptr(tokens), _ptr(window_len), B, gamma, V,
             ctypes.c_uint64(seed), ctypes.c_uint64(tag), _ptr(seq_ids), _ptr(base_pos),
             _ptr(out.n_accepted), _ptr(out.out_tokens), _ptr(out.p_draft), _ptr(out.q_draft),

@@ -100,6 +100,9 @@ size_t sv_workspace_size(int op, int32_t B, int32_t n, int32_t V, int dtype) {
     if (n < 1 || n > SV_MAX_GAMMA) return 0;
   } else if (op == SV_OP_TREE) {
     if (n < 1 || n > SV_TREE_MAX_NODES) return 0;
+  } else if (op == SV_OP_LMHEAD) {
+    if (n < 1 || n > SV_MAX_GAMMA || dtype != SV_DT_BF16) return 0;
+    return make_lm_layout(B, n, V).total;
   } else {
     return 0;
   }
@@ -429,6 +432,107 @@ int sv_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t str
   if (!src || !sink || bytes < 16 || bytes % 16 != 0 || bytes > (size_t(1) << 40) || !aligned(src, 16))
     return SV_EINVAL;
   launch_probe_read(src, bytes, sink, stream);
+  return launch_status();
+}
+
+int sv_verify_window_lmhead(const void *hidden_target, const void *unembed_target, int32_t Ht,
+                            const void *hidden_draft, const void *unembed_draft, int32_t Hd,
+                            const int32_t *draft_tokens, const int32_t *window_len,
+                            int32_t B, int32_t gamma, int32_t V,
+                            uint64_t seed, uint64_t tag, const uint64_t *seq_ids,
+                            const int64_t *base_pos,
+                            int32_t *n_accepted, int32_t *out_tokens,
+                            float *p_draft, float *q_draft,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (B < 1 || gamma < 1 || gamma > SV_MAX_GAMMA || V < 1 || V > kMaxVocab) return SV_EINVAL;
+  if (Ht < SV_LMHEAD_K_STEP || Hd < SV_LMHEAD_K_STEP || Ht % SV_LMHEAD_K_STEP || Hd % SV_LMHEAD_K_STEP ||
+      Ht > SV_LMHEAD_MAX_HIDDEN || Hd > SV_LMHEAD_MAX_HIDDEN)
+    return SV_EINVAL;
+  if (!hidden_target || !unembed_target || !hidden_draft || !unembed_draft || !draft_tokens || !n_accepted ||
+      !out_tokens)
+    return SV_EINVAL;
+  if (!aligned(hidden_target, 16) || !aligned(unembed_target, 16) || !aligned(hidden_draft, 16) ||
+      !aligned(unembed_draft, 16))
+    return SV_EINVAL;
+  const int64_t Mt = static_cast<int64_t>(B) * (gamma + 1), Md = static_cast<int64_t>(B) * gamma;
+  if (Mt + Md > (int64_t{1} << 30) || static_cast<int64_t>(lm_gemm_blocks(static_cast<int>(Mt), V)) > (1 << 30))
+    return SV_EINVAL;
+  const LmLayout L = make_lm_layout(B, gamma, V);
+  const int ws = check_workspace(workspace, workspace_bytes, L.total);
+  if (ws != SV_OK) return ws;
+  char *wsb = static_cast<char *>(workspace);
+  float2 *part = reinterpret_cast<float2 *>(wsb + L.part_off);
+  float2 *stats = reinterpret_cast<float2 *>(wsb + L.stats_off);
+  float *gath = reinterpret_cast<float *>(wsb + L.gath_off);
+  int32_t *idx = reinterpret_cast<int32_t *>(wsb + L.idx_off);
+  SampleJob *jobs = reinterpret_cast<SampleJob *>(wsb + L.jobs_off);
+  float *spart = reinterpret_cast<float *>(wsb + L.spart_off);
+  float *rows_t = reinterpret_cast<float *>(wsb + L.rows_t_off);
+  float *rows_d = reinterpret_cast<float *>(wsb + L.rows_d_off);
+
+  // pass 1: every target and draft row, statistics and the draft-token logits
+  LmGemmArgs G{};
+  G.A = static_cast<const uint16_t *>(hidden_target);
+  G.lda = Ht;
+  G.W = static_cast<const uint16_t *>(unembed_target);
+  G.M = static_cast<int32_t>(Mt);
+  G.V = V;
+  G.K = Ht;
+  G.part = part;
+  G.gath = gath;
+  G.tokens = draft_tokens;
+  G.gamma = gamma;
+  G.rows_per_seq = gamma + 1;
+  launch_lm_gemm(LM_STATS, G, stream);
+  LmGemmArgs Gd = G;
+  Gd.A = static_cast<const uint16_t *>(hidden_draft);
+  Gd.lda = Hd;
+  Gd.W = static_cast<const uint16_t *>(unembed_draft);
+  Gd.M = static_cast<int32_t>(Md);
+  Gd.K = Hd;
+  Gd.part = part + Mt * L.NT;
+  Gd.gath = gath + Mt;
+  Gd.rows_per_seq = gamma;
+  launch_lm_gemm(LM_STATS, Gd, stream);
+  launch_lm_combine(part, L.NT, static_cast<int>(Mt + Md), stats, stream);
+
+  LmDecideArgs D{};
+  D.stats_t = stats;
+  D.stats_d = stats + Mt;
+  D.gath_t = gath;
+  D.gath_d = gath + Mt;
+  D.tokens = draft_tokens;
+  D.window_len = window_len;
+  D.gamma = gamma;
+  D.V = V;
+  D.seed = seed;
+  D.tag = tag;
+  D.seq_ids = seq_ids;
+  D.base_pos = base_pos;
+  D.n_accepted = n_accepted;
+  D.out_tokens = out_tokens;
+  D.p_draft = p_draft;
+  D.q_draft = q_draft;
+  D.jobs = jobs;
+  D.rows_t = rows_t;
+  D.rows_d = rows_d;
+  D.idx_t = idx;
+  D.idx_d = idx + B;
+  launch_lm_decide(D, B, stream);
+
+  // pass 2: target row n and draft row n of every sequence, stored in float32
+  LmGemmArgs S = G;
+  S.a_rows = idx;
+  S.M = B;
+  S.out = rows_t;
+  launch_lm_gemm(LM_STORE, S, stream);
+  LmGemmArgs Sd = Gd;
+  Sd.a_rows = idx + B;
+  Sd.M = B;
+  Sd.out = rows_d;
+  launch_lm_gemm(LM_STORE, Sd, stream);
+
+  launch_tree_finish(SV_DT_F32, jobs, B, V, spart, L.cmax, stream);
   return launch_status();
 }
 

@@ -87,6 +87,44 @@ struct RollbackArgs {
   int32_t len_offset;
 };
 
+// LM-head fused window.  GEMM rows g < M: hidden row (a_rows ? a_rows[g] : g)
+// of A (row stride lda elements) against every row of W ([V][K], bf16).
+enum : int { LM_STATS = 0, LM_STORE = 1 };
+struct LmGemmArgs {
+  const uint16_t *A;
+  int64_t lda;
+  const int32_t *a_rows;
+  const uint16_t *W;
+  int32_t M, V, K;
+  int32_t RB, NT;             // row blocks, column tiles (set by the launcher)
+  float2 *part;               // STATS: [M][NT] (max, sum-exp) per row and column tile
+  float *gath;                // STATS: [M] logit at the row's draft token
+  const int32_t *tokens;      // STATS: [B][gamma]
+  int32_t gamma, rows_per_seq;
+  float *out;                 // STORE: [M][V] float32 logits
+};
+
+struct LmDecideArgs {
+  const float2 *stats_t, *stats_d;
+  const float *gath_t, *gath_d;
+  const int32_t *tokens;
+  const int32_t *window_len;
+  int32_t gamma, V;
+  uint64_t seed, tag;
+  const uint64_t *seq_ids;
+  const int64_t *base_pos;
+  int32_t *n_accepted, *out_tokens;
+  float *p_draft, *q_draft;
+  SampleJob *jobs;
+  const float *rows_t, *rows_d;  // where the second pass stores target / draft row n
+  int32_t *idx_t, *idx_d;        // hidden rows of that pass
+};
+
+void launch_lm_gemm(int mode, LmGemmArgs A, hipStream_t st);
+int lm_gemm_blocks(int M, int V);
+void launch_lm_combine(const float2 *part, int NT, int M, float2 *stats, hipStream_t st);
+void launch_lm_decide(const LmDecideArgs &A, int B, hipStream_t st);
+
 void launch_row_stats(int dtype, bool argmax, const RowSet &rs, int64_t blocks, float2 *part, hipStream_t st);
 void launch_window_finish(int dtype, const WindowArgs &A, int B, float *spart, int cmax, hipStream_t st);
 void launch_stage_decide(int dtype, const WindowArgs &A, int B, int lo, int hi, int32_t *status, hipStream_t st);

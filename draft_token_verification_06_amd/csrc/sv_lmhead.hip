@@ -1,0 +1,329 @@
+// LM head fused with verification (gfx950): logits = hidden x unembedding^T
+// on the matrix cores, consumed tile by tile by the row statistics, so the
+// logits never travel through HBM.  Only the rows a draw needs (target row n
+// and draft row n of each sequence) are recomputed by the same kernel and
+// stored, in float32, for the sampling pass.
+//
+// GEMM: C[M x V] = A[M x K] * W[V x K]^T, bf16 inputs, float32 accumulation in
+// v_mfma_f32_32x32x16_bf16.  Block tile 256 x 256, K step 64, 8 waves of 64 x
+// 128 (4 along M, 2 along V), double-buffered LDS, one barrier per K step.
+// Operand layout of the 32x32x16 instruction (checked on the device): lane l
+// supplies A[l % 32][8 (l / 32) + j] and W-row (l % 32) at the same k, j < 8;
+// accumulator register r of lane l is C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sv_device.h"
+#include "sv_launch.h"
+#include "sv_plan.h"
+
+namespace sv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kGemmThreads = 512;
+constexpr int kBM = 256;
+constexpr int kBN = kLmBN;
+constexpr int kBK = 64;
+constexpr int kLdsRow = kBK + 8;  // bf16 per LDS row: 16 bytes of padding spread the banks
+constexpr int kStageElems = (kBM + kBN) * kLdsRow;
+static_assert(kBN == 256, "the wave layout covers 256 columns");
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Block -> tile map: blocks are handed to the 8 XCDs round-robin, so blocks
+// L, L + 8, ... share an XCD; those get the row blocks of one column tile in
+// turn, and the unembedding tile is read from HBM once per XCD's L2.
+__device__ __forceinline__ bool lm_tile(int L, int RB, int NT, int *rb, int *ct) {
+  const int xcd = L & 7, slot = L >> 3;
+  *ct = xcd + 8 * (slot / RB);
+  *rb = slot % RB;
+  return *ct < NT;
+}
+
+template <int kMode>
+__global__ void __launch_bounds__(kGemmThreads) k_lm_gemm(LmGemmArgs P) {
+  __shared__ uint4 lds_raw[2 * kStageElems * sizeof(uint16_t) / sizeof(uint4)];
+  uint16_t *lds = reinterpret_cast<uint16_t *>(lds_raw);
+  __shared__ float2 s_red[2][kBM];
+  __shared__ int s_tok[kBM];
+  int rb, ct;
+  if (!lm_tile(blockIdx.x, P.RB, P.NT, &rb, &ct)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 3, wn = wave >> 2;
+  const int half = lane >> 5, c32 = lane & 31;
+  const int row0 = rb * kBM, col0 = ct * kBN;
+
+  // this thread's four A rows and four W rows of every K step (chunk q = tid + 512 j)
+  const uint4 *asrc[4], *wsrc[4];
+  bool aok[4], wok[4];
+  int lds_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = tid + kGemmThreads * j;
+    const int r = q >> 3, ch = q & 7;
+    const int gr = row0 + r, gc = col0 + r;
+    aok[j] = gr < P.M;
+    wok[j] = gc < P.V;
+    const int64_t arow = aok[j] ? (P.a_rows ? P.a_rows[gr] : gr) : 0;
+    asrc[j] = reinterpret_cast<const uint4 *>(P.A + arow * P.lda + ch * 8);
+    wsrc[j] = reinterpret_cast<const uint4 *>(P.W + static_cast<int64_t>(wok[j] ? gc : 0) * P.K + ch * 8);
+    lds_off[j] = r * kLdsRow + ch * 8;
+  }
+  if (kMode == LM_STATS && tid < kBM) {
+    const int g = row0 + tid;
+    int x = -1;
+    if (g < P.M) {
+      const int b = g / P.rows_per_seq, i = g - b * P.rows_per_seq;
+      if (i < P.gamma) x = P.tokens[static_cast<int64_t>(b) * P.gamma + i];
+    }
+    s_tok[tid] = x;
+  }
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mt][nt][e] = 0.0f;
+
+  // rows past M or V load row 0 and are masked to zero, word by word
+  uint32_t amask[4], wmask[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    amask[j] = aok[j] ? 0xFFFFFFFFu : 0u;
+    wmask[j] = wok[j] ? 0xFFFFFFFFu : 0u;
+  }
+  uint4 ra[4], rw[4];
+#define SV_LM_FETCH(k0)                                                                  \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                        \
+    const uint4 a_ = load_vec(asrc[j] + (k0) / 8);                                       \
+    const uint4 w_ = load_vec(wsrc[j] + (k0) / 8);                                       \
+    ra[j] = make_uint4(a_.x & amask[j], a_.y & amask[j], a_.z & amask[j], a_.w & amask[j]); \
+    rw[j] = make_uint4(w_.x & wmask[j], w_.y & wmask[j], w_.z & wmask[j], w_.w & wmask[j]); \
+  }
+#define SV_LM_STASH(st)                                                    \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j) {                          \
+    uint16_t *sa_ = lds + (st) * kStageElems;                              \
+    *reinterpret_cast<uint4 *>(sa_ + lds_off[j]) = ra[j];                  \
+    *reinterpret_cast<uint4 *>(sa_ + kBM * kLdsRow + lds_off[j]) = rw[j];  \
+  }
+
+  const int nk = P.K / kBK;
+  SV_LM_FETCH(0)
+  SV_LM_STASH(0)
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) {
+      SV_LM_FETCH((kt + 1) * kBK)
+    }
+    const uint16_t *sa = lds + st * kStageElems + (wm * 64 + c32) * kLdsRow + 8 * half;
+    const uint16_t *sw = lds + st * kStageElems + kBM * kLdsRow + (wn * 128 + c32) * kLdsRow + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      bf16x8_t a[2], w[4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        a[mt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sa + mt * 32 * kLdsRow + ks * 16));
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        w[nt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sw + nt * 32 * kLdsRow + ks * 16));
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], w[nt], acc[mt][nt], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      SV_LM_STASH(st ^ 1)
+    }
+    __syncthreads();
+  }
+#undef SV_LM_FETCH
+#undef SV_LM_STASH
+
+  if (kMode == LM_STORE) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int g = row0 + wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (g >= P.M) continue;
+        float *orow = P.out + static_cast<int64_t>(g) * P.V;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int col = col0 + wn * 128 + nt * 32 + c32;
+          if (col < P.V) orow[col] = acc[mt][nt][r];
+        }
+      }
+    return;
+  }
+
+  // Row statistics of this wave's 128 columns: max, then sum of exp(x - max)
+  // (the same 2^(x log2e - m log2e) form as the streaming row pass), across
+  // the 32 lanes of each half-wave; the draft token's logit is picked up by
+  // the lane holding its column.
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rl = wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      float v[4];
+      float m = kNegInf;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int col = col0 + wn * 128 + nt * 32 + c32;
+        v[nt] = col < P.V ? acc[mt][nt][r] : kNegInf;
+        m = fmaxf(m, v[nt]);
+      }
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+      float s = 0.0f;
+      if (m != kNegInf) {
+        const float ml = m * kLog2e;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) s += exp_shift(v[nt], ml);
+      }
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) s += __shfl_xor(s, off);
+      const int x = s_tok[rl];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int col = col0 + wn * 128 + nt * 32 + c32;
+        if (col == x) P.gath[row0 + rl] = acc[mt][nt][r];
+      }
+      if (c32 == 0) s_red[wn][rl] = make_float2(m, s);
+    }
+  __syncthreads();
+  if (tid < kBM && row0 + tid < P.M) {
+    const float2 p0 = s_red[0][tid], p1 = s_red[1][tid];
+    const MaxSum c = combine(MaxSum{p0.x, p0.y}, MaxSum{p1.x, p1.y});
+    P.part[static_cast<int64_t>(row0 + tid) * P.NT + ct] = make_float2(c.m, c.s);
+  }
+}
+
+// Per row, the column-tile partials in a fixed order: lane-strided, then the
+// wave butterfly.  One wave per row.
+__global__ void __launch_bounds__(256) k_lm_combine(const float2 *__restrict__ part, int NT, int M,
+                                                    float2 *__restrict__ stats) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  MaxSum a{kNegInf, 0.0f};
+  const float2 *p = part + static_cast<int64_t>(row) * NT;
+  for (int c = lane; c < NT; c += kWave) {
+    const float2 q = p[c];
+    a = combine(a, MaxSum{q.x, q.y});
+  }
+  a = wave_reduce(a);
+  if (lane == 0) stats[row] = make_float2(a.m, a.s);
+}
+
+__device__ __forceinline__ float lm_prob(float x, float2 st) {
+  return exp_shift(x, st.x * kLog2e) / st.y;
+}
+__device__ __forceinline__ float lm_offset(float2 st) { return st.x * kLog2e + log2f(st.y); }
+
+// Window decision from the fused statistics (one wave per sequence, lane i =
+// position i): p_i(x_i), q_i(x_i) from the row statistics and the logits at the
+// draft tokens; accept iff u q < p; the first rejection ends the window.
+// Writes the window outputs, the sampling job (rows in the workspace, filled
+// by the second GEMM pass) and the hidden-state rows that pass needs.
+__global__ void __launch_bounds__(kWave) k_lm_decide(LmDecideArgs A) {
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const int g = A.gamma;
+  int32_t *out = A.out_tokens + static_cast<int64_t>(b) * (g + 1);
+  const int len = A.window_len ? A.window_len[b] : g;
+  const bool bad_len = len < 0 || len > g;
+  const int x = i < g ? A.tokens[static_cast<int64_t>(b) * g + i] : 0;
+  const bool bad_tok = !bad_len && i < len && (x < 0 || x >= A.V);
+  if (__any(bad_len || bad_tok)) {
+    for (int k = i; k <= g; k += kWave) out[k] = -1;
+    for (int k = i; k < g; k += kWave) {
+      if (A.p_draft) A.p_draft[static_cast<int64_t>(b) * g + k] = 0.0f;
+      if (A.q_draft) A.q_draft[static_cast<int64_t>(b) * g + k] = 0.0f;
+    }
+    if (i == 0) {
+      A.n_accepted[b] = -1;
+      A.jobs[b].mode = JOB_NONE;
+      A.idx_t[b] = b * (g + 1);
+      A.idx_d[b] = b * g;
+    }
+    return;
+  }
+  const uint64_t seq = A.seq_ids ? A.seq_ids[b] : static_cast<uint64_t>(b);
+  const int64_t base = A.base_pos ? A.base_pos[b] : 0;
+  const int64_t rt = static_cast<int64_t>(b) * (g + 1), rd = static_cast<int64_t>(b) * g;
+  const U64x4 w = philox4x64_10({seq, static_cast<uint64_t>(base + 1 + i), 0, 0}, A.seed, A.tag);
+  float P = 0.0f, Q = 0.0f;
+  bool acc = false;
+  if (i < len) {
+    P = lm_prob(A.gath_t[rt + i], A.stats_t[rt + i]);
+    Q = lm_prob(A.gath_d[rd + i], A.stats_d[rd + i]);
+    acc = uniform24(w.c0) * Q < P;
+  }
+  const uint64_t inv = ~static_cast<uint64_t>(__ballot(acc));
+  int n = inv ? __builtin_ctzll(inv) : kWave;
+  n = min(n, len);
+  if (i < g) {
+    if (A.p_draft) A.p_draft[rd + i] = P;
+    if (A.q_draft) A.q_draft[rd + i] = Q;
+  }
+  for (int k = i; k <= g; k += kWave)
+    if (k != n) out[k] = k < n ? A.tokens[rd + k] : -1;
+  float v = __shfl(uniform24(w.c1), n & (kWave - 1));
+  if (i == 0) {
+    if (n >= kWave) {  // gamma = 64 with every draft accepted: position 64 has no lane
+      const U64x4 w2 = philox4x64_10({seq, static_cast<uint64_t>(base + 1 + n), 0, 0}, A.seed, A.tag);
+      v = uniform24(w2.c1);
+    }
+    SampleJob jb{};
+    jb.t_row = A.rows_t + static_cast<int64_t>(b) * A.V;
+    jb.ct = lm_offset(A.stats_t[rt + n]);
+    if (n < len) {
+      jb.mode = JOB_RESIDUAL;
+      jb.d_row = A.rows_d + static_cast<int64_t>(b) * A.V;
+      jb.cd = lm_offset(A.stats_d[rd + n]);
+      jb.cq = 1.0f;
+    } else {
+      jb.mode = JOB_BONUS;
+      jb.d_row = nullptr;
+    }
+    jb.v = v;
+    jb.out_slot = out + n;
+    A.jobs[b] = jb;
+    A.n_accepted[b] = n;
+    A.idx_t[b] = static_cast<int32_t>(rt + n);
+    A.idx_d[b] = static_cast<int32_t>(rd + min(n, g - 1));
+  }
+}
+
+int lm_gemm_blocks(int M, int V) {
+  const int RB = (M + kBM - 1) / kBM, NT = (V + kBN - 1) / kBN;
+  return 8 * ((NT + 7) / 8) * RB;
+}
+
+void launch_lm_gemm(int mode, LmGemmArgs A, hipStream_t st) {
+  A.RB = (A.M + kBM - 1) / kBM;
+  A.NT = (A.V + kBN - 1) / kBN;
+  const int blocks = lm_gemm_blocks(A.M, A.V);
+  if (mode == LM_STATS)
+    hipLaunchKernelGGL(k_lm_gemm<LM_STATS>, dim3(blocks), dim3(kGemmThreads), 0, st, A);
+  else
+    hipLaunchKernelGGL(k_lm_gemm<LM_STORE>, dim3(blocks), dim3(kGemmThreads), 0, st, A);
+}
+
+void launch_lm_combine(const float2 *part, int NT, int M, float2 *stats, hipStream_t st) {
+  hipLaunchKernelGGL(k_lm_combine, dim3((M + 3) / 4), dim3(256), 0, st, part, NT, M, stats);
+}
+
+void launch_lm_decide(const LmDecideArgs &A, int B, hipStream_t st) {
+  hipLaunchKernelGGL(k_lm_decide, dim3(B), dim3(kWave), 0, st, A);
+}
+
+}  // namespace sv

@@ -62,6 +62,9 @@ struct TreeMeta {
 };
 static_assert(sizeof(TreeMeta) <= 2560, "tree metadata travels in the kernel arguments");
 
+// LM-head fused path: vocabulary columns per GEMM block tile.
+constexpr int kLmBN = 256;
+
 struct RowPlan {
   int S;        // segments per row
   int seg_len;  // elements per segment (multiple of 8)
@@ -107,6 +110,40 @@ inline Layout make_layout(int op, int64_t B, int32_t n, int32_t V) {
   off = align256(off + sizeof(float) * static_cast<size_t>(B) * L.cmax);
   L.status_off = off;  // early-exit window: per-sequence status
   off = align256(off + (op == 0 ? sizeof(int32_t) * static_cast<size_t>(B) : 0));
+  L.total = off;
+  return L;
+}
+
+// Workspace of the LM-head fused window (byte offsets).  Rows: B(gamma+1)
+// target rows then B gamma draft rows.
+struct LmLayout {
+  int NT;  // column tiles
+  int cmax;
+  size_t part_off, stats_off, gath_off, idx_off, jobs_off, spart_off, rows_t_off, rows_d_off, total;
+};
+
+inline LmLayout make_lm_layout(int64_t B, int32_t gamma, int32_t V) {
+  LmLayout L{};
+  const int64_t Mt = B * (gamma + 1), Md = B * gamma, M = Mt + Md;
+  L.NT = (V + kLmBN - 1) / kLmBN;
+  L.cmax = fin_chunks_max(V);
+  size_t off = 0;
+  L.part_off = off;
+  off = align256(off + sizeof(float) * 2 * static_cast<size_t>(M) * L.NT);
+  L.stats_off = off;
+  off = align256(off + sizeof(float) * 2 * static_cast<size_t>(M));
+  L.gath_off = off;
+  off = align256(off + sizeof(float) * static_cast<size_t>(M));
+  L.idx_off = off;
+  off = align256(off + sizeof(int32_t) * 2 * static_cast<size_t>(B));
+  L.jobs_off = off;
+  off = align256(off + sizeof(SampleJob) * static_cast<size_t>(B));
+  L.spart_off = off;
+  off = align256(off + sizeof(float) * static_cast<size_t>(B) * L.cmax);
+  L.rows_t_off = off;
+  off = align256(off + sizeof(float) * static_cast<size_t>(B) * V);
+  L.rows_d_off = off;
+  off = align256(off + sizeof(float) * static_cast<size_t>(B) * V);
   L.total = off;
   return L;
 }

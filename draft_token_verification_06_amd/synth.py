@@ -159,6 +159,30 @@ def hierarchy_config4(S=64, V=128256, gamma1=8, mode="greedy", seed=1004, device
             "gamma1": gamma1}
 
 
+def lmhead_batch(B, gamma, V, Ht, Hd, logit_sd=3.0, noise=0.5, seed=0, device="cpu"):
+    """Hidden states and unembeddings (bf16) for the LM-head window.
+
+    Target: hidden rows ~ N(0, 1) of width Ht, unembedding rows ~ N(0, sd^2 / Ht)
+    (logits of standard deviation ~logit_sd).  Draft (width Hd <= Ht): its
+    unembedding is the target's first Hd columns rescaled by sqrt(Ht / Hd), its
+    hidden rows the target's first Hd entries plus N(0, noise^2), so draft and
+    target logits are correlated.  Draft tokens are drawn from the draft's own
+    logits (computed here in float32 from the rounded inputs)."""
+    if Hd > Ht:
+        raise ValueError("the draft's hidden width must not exceed the target's")
+    g = generator(seed, device)
+    h_t = _normal((B, gamma + 1, Ht), 1.0, g, device).to(torch.bfloat16)
+    w_t = _normal((V, Ht), logit_sd / Ht ** 0.5, g, device).to(torch.bfloat16)
+    h_d = (h_t[:, :gamma, :Hd].to(torch.float32) + _normal((B, gamma, Hd), noise, g, device)
+           ).to(torch.bfloat16).contiguous()
+    w_d = (w_t[:, :Hd].to(torch.float32) * (Ht / Hd) ** 0.5).to(torch.bfloat16).contiguous()
+    D = (h_d.to(torch.float32).reshape(-1, Hd) @ w_d.to(torch.float32).T).reshape(B, gamma, V)
+    tokens = gumbel_max_tokens(D, g)
+    del D
+    return {"h_target": h_t, "w_target": w_t, "h_draft": h_d, "w_draft": w_d, "tokens": tokens,
+            "B": B, "gamma": gamma, "V": V, "Ht": Ht, "Hd": Hd}
+
+
 def alpha_exact_probs(alpha, V, rng):
     """(p, q) with sum_k min(p_k, q_k) == alpha exactly.
 

@@ -68,12 +68,14 @@ typedef enum {
   SV_ELAUNCH = -5     /* a kernel launch failed                                */
 } sv_status;
 
-typedef enum { SV_OP_WINDOW = 0, SV_OP_GREEDY = 1, SV_OP_TREE = 2 } sv_op;
+typedef enum { SV_OP_WINDOW = 0, SV_OP_GREEDY = 1, SV_OP_TREE = 2, SV_OP_LMHEAD = 3 } sv_op;
 
 typedef enum { SV_TREE_GREEDY = 0, SV_TREE_STOCHASTIC = 1, SV_TREE_MULTI_CANDIDATE = 2 } sv_tree_mode;
 
 #define SV_MAX_GAMMA 64
 #define SV_TREE_MAX_NODES 256
+#define SV_LMHEAD_K_STEP 64
+#define SV_LMHEAD_MAX_HIDDEN 65536
 #define SV_TREE_MAX_DEPTH 64
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
@@ -235,6 +237,35 @@ int sv_rollback(int32_t *buf_tokens, int32_t *buf_len, int32_t S, int32_t K,
  * bandwidth ceiling of the running GPU. */
 int32_t sv_probe_blocks(size_t bytes);
 int sv_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+
+/* Speculative-sampling window on logits produced from hidden states, with
+ * the LM head fused into the verification: the same rule and outputs as
+ * sv_verify_window, where the logits are
+ *   target row i of sequence b = hidden_target[b][i] . unembed_target[k] for k < V,
+ *   draft  row i of sequence b = hidden_draft[b][i]  . unembed_draft[k],
+ * dot products of bf16 values accumulated in float32 on the matrix cores.
+ * The logits never go to memory: each GEMM tile feeds the row statistics and
+ * the logits at the draft tokens directly.  The rows a draw needs (target row
+ * n and draft row n of each sequence) are recomputed by the same tiles and
+ * stored in float32 in the workspace.  This is an extension beyond the pages,
+ * which only say that draft and target models produce the distributions.
+ *   hidden_target [B][gamma+1][Ht] bf16, unembed_target [V][Ht] bf16,
+ *   hidden_draft  [B][gamma][Hd]   bf16, unembed_draft  [V][Hd] bf16; dense,
+ *   16-byte aligned; Ht, Hd multiples of SV_LMHEAD_K_STEP, at most
+ *   SV_LMHEAD_MAX_HIDDEN.
+ *   Other arguments and outputs as sv_verify_window; workspace of
+ *   sv_workspace_size(SV_OP_LMHEAD, B, gamma, V, SV_DT_BF16) bytes (it holds two
+ *   float32 vocabulary rows per sequence).
+ * Errors: as sv_verify_window; SV_EINVAL for hidden sizes outside the rules. */
+int sv_verify_window_lmhead(const void *hidden_target, const void *unembed_target, int32_t Ht,
+                            const void *hidden_draft, const void *unembed_draft, int32_t Hd,
+                            const int32_t *draft_tokens, const int32_t *window_len,
+                            int32_t B, int32_t gamma, int32_t V,
+                            uint64_t seed, uint64_t tag, const uint64_t *seq_ids,
+                            const int64_t *base_pos,
+                            int32_t *n_accepted, int32_t *out_tokens,
+                            float *p_draft, float *q_draft,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

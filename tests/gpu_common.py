@@ -198,3 +198,57 @@ def check_tree_walk(data, res, *, seed=0, tag=0, seq_ids=None, base_pos=None, ro
             assert _walk_decision_margin(o["tests"]), (b, list(nodes_gpu[b]), want_n)
         margins += 1
     return len(rows), margins, rejected
+
+
+def lmhead_logit_tol(logits, K):
+    """Error allowance of float32 logits accumulated over K bf16 products in
+    K/16 matrix-core steps: a random walk of K/16 roundings (unit 2^-24) of
+    partial sums no larger than the row's largest |logit|, taken 4 times."""
+    return 4.0 * 2.0 ** -24 * np.sqrt(K / 16.0) * float(np.max(np.abs(logits)))
+
+
+def check_lmhead(data, res, *, seed, tag=0, window_len=None, rows=None):
+    """Compares sv_verify_window_lmhead with oracle.verify_window_lmhead on the
+    sequences `rows`.  Tolerances: the window's (1e-5) plus twice the logit
+    allowance of lmhead_logit_tol (token logit and log-normaliser both carry
+    it).  Returns (n_checked, n_margin_cases)."""
+    gamma, B = data["gamma"], data["B"]
+    rows = range(B) if rows is None else rows
+    Wt = host_rows(data["w_target"], "bf16")
+    Wd = host_rows(data["w_draft"], "bf16")
+    Kt, Kd = Wt.shape[1], Wd.shape[1]
+    n_gpu = res.n_accepted.cpu().numpy()
+    out_gpu = res.out_tokens.cpu().numpy()
+    P_gpu = res.p_draft.cpu().numpy() if res.p_draft is not None else None
+    Q_gpu = res.q_draft.cpu().numpy() if res.q_draft is not None else None
+    toks = data["tokens"].cpu().numpy()
+    wl = window_len.cpu().numpy() if window_len is not None else None
+    margins = 0
+    for b in rows:
+        T = oracle.lmhead_logits(host_rows(data["h_target"][b], "bf16"), Wt)
+        D = oracle.lmhead_logits(host_rows(data["h_draft"][b], "bf16"), Wd)
+        tp = PROB_RTOL + 2 * lmhead_logit_tol(T, Kt)
+        tq = PROB_RTOL + 2 * lmhead_logit_tol(D, Kd)
+        length = int(wl[b]) if wl is not None else gamma
+        u, v = oracle.window_uniforms(seed, tag, b, 0, gamma)
+        o = oracle.verify_window(T, D, toks[b], length, u, v)
+        if P_gpu is not None:
+            for i in range(min(o["n"] + 1, length)):
+                assert abs(P_gpu[b, i] - o["P"][i]) <= tp * o["P"][i], (b, i, P_gpu[b, i], o["P"][i], tp)
+                assert abs(Q_gpu[b, i] - o["Q"][i]) <= tq * o["Q"][i], (b, i, Q_gpu[b, i], o["Q"][i], tq)
+        ng = int(n_gpu[b])
+        want = o["out"] + [-1] * (gamma + 1 - len(o["out"]))
+        if ng == o["n"] and list(out_gpu[b]) == want:
+            continue
+        if ng != o["n"]:
+            near = any(np.isfinite(r) and abs(o["u"][i] - r) < MARGIN + (tp + tq) * r
+                       for i, r in enumerate(o["ratio"][: min(ng, o["n"]) + 1]))
+            assert near, (b, ng, o["n"], list(out_gpu[b]), o["out"])
+        else:
+            assert list(out_gpu[b][:ng]) == o["out"][:ng]
+            s = o["sample"]
+            tol = MARGIN + 2 * (tp + tq)
+            assert abs(s["tau"] - s["C_lo"]) / s["Z"] < tol or abs(s["tau"] - s["C_hi"]) / s["Z"] < tol, \
+                (b, list(out_gpu[b]), o["out"], s)
+        margins += 1
+    return len(rows), margins

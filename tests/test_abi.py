@@ -103,6 +103,18 @@ def test_bad_host_arguments_return_status_without_device_work():
                             fake, fake, fake, fake, fake, 1 << 20, None) == -1
     assert L.sv_verify_tree(fake, fake, 1, fake, par, 1, 3, 100, 3, 0, 0, None, None,
                             fake, fake, fake, fake, fake, 1 << 20, None) == -1
+    # LM-head window: hidden width not a multiple of 64, null unembedding, small workspace
+    assert L.sv_verify_window_lmhead(fake, fake, 100, fake, fake, 64, fake, None, 1, 4, 100,
+                                     0, 0, None, None, fake, fake, None, None,
+                                     fake, 1 << 30, None) == -1
+    assert L.sv_verify_window_lmhead(fake, None, 64, fake, fake, 64, fake, None, 1, 4, 100,
+                                     0, 0, None, None, fake, fake, None, None,
+                                     fake, 1 << 30, None) == -1
+    assert L.sv_verify_window_lmhead(fake, fake, 64, fake, fake, 64, fake, None, 1, 4, 100,
+                                     0, 0, None, None, fake, fake, None, None,
+                                     fake, 16, None) == -3
+    assert L.sv_workspace_size(3, 4, 8, 1000, 0) == 0  # LM-head workspace is for bf16 only
+    assert L.sv_workspace_size(3, 4, 8, 1000, 1) > 2 * 4 * 1000 * 4
     # rollback: stage outside [1, K-1], null buffers
     assert L.sv_rollback(fake, fake, 4, 3, 8, 3, fake, 8, fake, 0, None) == -1
     assert L.sv_rollback(fake, fake, 4, 3, 8, 0, fake, 8, fake, 0, None) == -1
