@@ -64,6 +64,8 @@ def parse():
 def event_time_ms(torch, fn, reps):
     """Average duration of fn() over reps launches, HIP events around each."""
     s = torch.cuda.current_stream()
+    for _ in range(2):  # warm-up: first-call set-up of the libraries involved
+        fn()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
     for a, b in ev:
@@ -349,6 +351,31 @@ def side_workloads(torch, sv, synth, dev):
     out["tree_432_B32_V50257_f16_sigma2_multi_candidate"] = {
         "us": ms * 1e3, "mean_depth": float(r.n_accepted.float().mean().item())}
     del d, w
+
+    # LM head fused with the window (8B-shaped target Ht=4096, 1B-shaped draft Hd=2048)
+    Bl, Ht, Hd = 256, 4096, 2048
+    d = synth.lmhead_batch(Bl, GAMMA, V, Ht, Hd, seed=2024, device=dev)
+    w = sv.workspace(sv.SV_OP_LMHEAD, Bl, GAMMA, V, torch.bfloat16, dev)
+    f_ms = event_time_ms(torch, lambda: sv.verify_window_lmhead(d["h_target"], d["w_target"], d["h_draft"],
+                                                                d["w_draft"], d["tokens"], ws=w), 10)
+    del w
+    ht, hd = d["h_target"].view(-1, Ht), d["h_draft"].view(-1, Hd)
+    lt = torch.empty(Bl * (GAMMA + 1), V, dtype=torch.bfloat16, device=dev)
+    ld = torch.empty(Bl * GAMMA, V, dtype=torch.bfloat16, device=dev)
+    wsw = sv.workspace(sv.SV_OP_WINDOW, Bl, GAMMA, V, torch.bfloat16, dev)
+
+    def unfused():
+        torch.matmul(ht, d["w_target"].t(), out=lt)
+        torch.matmul(hd, d["w_draft"].t(), out=ld)
+        sv.verify_window(lt.view(Bl, GAMMA + 1, V), ld.view(Bl, GAMMA, V), d["tokens"], ws=wsw)
+
+    u_ms = event_time_ms(torch, unfused, 10)
+    flops = 2 * (Bl * (GAMMA + 1) * Ht + Bl * GAMMA * Hd) * V + 2 * Bl * (Ht + Hd) * V
+    out["lmhead_fused_B256_g8_V128256_Ht4096_Hd2048"] = {
+        "us": f_ms * 1e3, "TFLOPs": flops / (f_ms * 1e-3) / 1e12,
+        "frac_of_bf16_mfma_peak": flops / (f_ms * 1e-3) / 2.5e15,
+        "unfused_hipblaslt_gemm_plus_window_us": u_ms * 1e3}
+    del d, lt, ld, wsw
 
     # PipeSpec-shaped hierarchy, 64 streams: stage-1 window, rollback, stage-2 window, rollback
     h = synth.hierarchy_config4(S=64, mode="stochastic", device=dev)

@@ -22,10 +22,19 @@ namespace sv {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kGemmThreads = 512;
-constexpr int kBM = 256;
-constexpr int kBN = kLmBN;
-constexpr int kBK = 64;
+#ifndef SV_LM_BM
+#define SV_LM_BM 256
+#endif
+#ifndef SV_LM_BK
+#define SV_LM_BK 64
+#endif
+constexpr int kBM = SV_LM_BM;              // rows per block: kBM / 64 waves along M
+constexpr int kBN = kLmBN;                 // 2 waves along V, 128 columns each
+constexpr int kBK = SV_LM_BK;
+constexpr int kGemmThreads = 2 * kBM;
+constexpr int kChunksK = kBK / 8;          // 16-byte chunks per row and K step
+constexpr int kLoadsA = kBM * kChunksK / kGemmThreads;
+constexpr int kLoadsW = kBN * kChunksK / kGemmThreads;
 constexpr int kLdsRow = kBK + 8;  // bf16 per LDS row: 16 bytes of padding spread the banks
 constexpr int kStageElems = (kBM + kBN) * kLdsRow;
 static_assert(kBN == 256, "the wave layout covers 256 columns");
@@ -43,7 +52,8 @@ __device__ __forceinline__ bool lm_tile(int L, int RB, int NT, int *rb, int *ct)
 }
 
 template <int kMode>
-__global__ void __launch_bounds__(kGemmThreads) k_lm_gemm(LmGemmArgs P) {
+__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)))
+k_lm_gemm(LmGemmArgs P) {
   __shared__ uint4 lds_raw[2 * kStageElems * sizeof(uint16_t) / sizeof(uint4)];
   uint16_t *lds = reinterpret_cast<uint16_t *>(lds_raw);
   __shared__ float2 s_red[2][kBM];
@@ -52,25 +62,29 @@ __global__ void __launch_bounds__(kGemmThreads) k_lm_gemm(LmGemmArgs P) {
   if (!lm_tile(blockIdx.x, P.RB, P.NT, &rb, &ct)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 3, wn = wave >> 2;
+  const int wm = wave % (kBM / 64), wn = wave / (kBM / 64);
   const int half = lane >> 5, c32 = lane & 31;
   const int row0 = rb * kBM, col0 = ct * kBN;
 
-  // this thread's four A rows and four W rows of every K step (chunk q = tid + 512 j)
-  const uint4 *asrc[4], *wsrc[4];
-  bool aok[4], wok[4];
-  int lds_off[4];
+  // this thread's A and W chunks of every K step (chunk q = tid + threads * j)
+  const uint4 *asrc[kLoadsA], *wsrc[kLoadsW];
+  int aoff[kLoadsA], woff[kLoadsW];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kLoadsA; ++j) {
     const int q = tid + kGemmThreads * j;
-    const int r = q >> 3, ch = q & 7;
-    const int gr = row0 + r, gc = col0 + r;
-    aok[j] = gr < P.M;
-    wok[j] = gc < P.V;
-    const int64_t arow = aok[j] ? (P.a_rows ? P.a_rows[gr] : gr) : 0;
+    const int r = q / kChunksK, ch = q % kChunksK;
+    const int gr = row0 + r;
+    const int64_t arow = gr < P.M ? (P.a_rows ? P.a_rows[gr] : gr) : 0;
     asrc[j] = reinterpret_cast<const uint4 *>(P.A + arow * P.lda + ch * 8);
-    wsrc[j] = reinterpret_cast<const uint4 *>(P.W + static_cast<int64_t>(wok[j] ? gc : 0) * P.K + ch * 8);
-    lds_off[j] = r * kLdsRow + ch * 8;
+    aoff[j] = r * kLdsRow + ch * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < kLoadsW; ++j) {
+    const int q = tid + kGemmThreads * j;
+    const int r = q / kChunksK, ch = q % kChunksK;
+    const int gc = col0 + r;
+    wsrc[j] = reinterpret_cast<const uint4 *>(P.W + static_cast<int64_t>(gc < P.V ? gc : 0) * P.K + ch * 8);
+    woff[j] = kBM * kLdsRow + r * kLdsRow + ch * 8;
   }
   if (kMode == LM_STATS && tid < kBM) {
     const int g = row0 + tid;
@@ -90,32 +104,25 @@ __global__ void __launch_bounds__(kGemmThreads) k_lm_gemm(LmGemmArgs P) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mt][nt][e] = 0.0f;
 
-  // rows past M or V load row 0 and are masked to zero, word by word
-  uint32_t amask[4], wmask[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    amask[j] = aok[j] ? 0xFFFFFFFFu : 0u;
-    wmask[j] = wok[j] ? 0xFFFFFFFFu : 0u;
-  }
-  uint4 ra[4], rw[4];
-#define SV_LM_FETCH(k0)                                                                  \
-  _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                        \
-    const uint4 a_ = load_vec(asrc[j] + (k0) / 8);                                       \
-    const uint4 w_ = load_vec(wsrc[j] + (k0) / 8);                                       \
-    ra[j] = make_uint4(a_.x & amask[j], a_.y & amask[j], a_.z & amask[j], a_.w & amask[j]); \
-    rw[j] = make_uint4(w_.x & wmask[j], w_.y & wmask[j], w_.z & wmask[j], w_.w & wmask[j]); \
-  }
-#define SV_LM_STASH(st)                                                    \
-  _Pragma("unroll") for (int j = 0; j < 4; ++j) {                          \
-    uint16_t *sa_ = lds + (st) * kStageElems;                              \
-    *reinterpret_cast<uint4 *>(sa_ + lds_off[j]) = ra[j];                  \
-    *reinterpret_cast<uint4 *>(sa_ + kBM * kLdsRow + lds_off[j]) = rw[j];  \
-  }
+  // Rows past M (A) or V (W) load row 0, in bounds; their products land in
+  // accumulator rows that are never stored and columns the epilogues mask.
+  uint4 ra[kLoadsA], rw[kLoadsW];
+#define SV_LM_FETCH(k0)                                                                   \
+  _Pragma("unroll") for (int j = 0; j < kLoadsA; ++j) ra[j] = load_vec(asrc[j] + (k0) / 8); \
+  _Pragma("unroll") for (int j = 0; j < kLoadsW; ++j) rw[j] = load_vec(wsrc[j] + (k0) / 8);
+#define SV_LM_STASH(st)                                                                              \
+  _Pragma("unroll") for (int j = 0; j < kLoadsA; ++j)                                                \
+      *reinterpret_cast<uint4 *>(lds + (st) * kStageElems + aoff[j]) = ra[j];                        \
+  _Pragma("unroll") for (int j = 0; j < kLoadsW; ++j)                                                \
+      *reinterpret_cast<uint4 *>(lds + (st) * kStageElems + woff[j]) = rw[j];
 
   const int nk = P.K / kBK;
   SV_LM_FETCH(0)
   SV_LM_STASH(0)
   __syncthreads();
+#ifndef SV_LM_PIPE
+#define SV_LM_PIPE 1
+#endif
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
     if (kt + 1 < nk) {
@@ -123,6 +130,35 @@ __global__ void __launch_bounds__(kGemmThreads) k_lm_gemm(LmGemmArgs P) {
     }
     const uint16_t *sa = lds + st * kStageElems + (wm * 64 + c32) * kLdsRow + 8 * half;
     const uint16_t *sw = lds + st * kStageElems + kBM * kLdsRow + (wn * 128 + c32) * kLdsRow + 8 * half;
+#if SV_LM_PIPE
+    // operands of K sub-step ks + 1 are read while sub-step ks multiplies; the
+    // next tile goes to the other LDS stage in the middle of the step
+    bf16x8_t a[2][2], w[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) a[0][mt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sa + mt * 32 * kLdsRow));
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) w[0][nt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sw + nt * 32 * kLdsRow));
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int cur = ks & 1, nxt = cur ^ 1;
+      if (ks + 1 < kBK / 16) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          a[nxt][mt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sa + mt * 32 * kLdsRow + (ks + 1) * 16));
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          w[nxt][nt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sw + nt * 32 * kLdsRow + (ks + 1) * 16));
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mt], w[cur][nt], acc[mt][nt], 0, 0, 0);
+      if (ks == (kBK / 16) / 2 - 1 && kt + 1 < nk) {
+        SV_LM_STASH(st ^ 1)
+      }
+    }
+#else
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       bf16x8_t a[2], w[4];
@@ -141,6 +177,7 @@ __global__ void __launch_bounds__(kGemmThreads) k_lm_gemm(LmGemmArgs P) {
     if (kt + 1 < nk) {
       SV_LM_STASH(st ^ 1)
     }
+#endif
     __syncthreads();
   }
 #undef SV_LM_FETCH
