@@ -30,6 +30,16 @@ ALPHAS = (0.05, 0.3, 0.6, 0.9)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "verified draft tokens/s + achieved HBM GB/s, γ=8 window, vocab 128256 bf16"
 HERE = os.path.dirname(os.path.abspath(__file__))
+# End-to-end decoding speedups the pages report (context only; they need
+# trained models and datasets, and are not comparable with a kernel rate).
+CONTEXT_PAGES = [
+    {"page": "PipeSpec (Pith review)", "speedup": "up to 2.54x vs autoregressive",
+     "setup": "LLaMA-3.1 {1B, 8B, 70B}, HumanEval, greedy; 4 A100 GPUs (70B on 2), baseline on 2"},
+    {"page": "Accelerating LLM Inference with Staged Speculative Decoding", "speedup": "3.16x lower latency",
+     "setup": "GPT-2-L (762M), single batch, small-batch on-device; hardware not stated"},
+    {"page": "CLaSp (Pith review)", "speedup": "1.3x-1.7x",
+     "setup": "LLaMA3 series, Spec-Bench; hardware not stated"},
+]
 KERNEL_SOURCES = ("sv_kernels.hip", "sv_device.h", "sv_plan.h")
 
 # HBM bytes per launch of the row-statistics kernel on this workload, from
@@ -123,6 +133,30 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
+    # The same calls with consecutive steps alternating over two streams
+    # (default priority, a workspace and outputs each): a step's draw overlaps
+    # the next step's row pass.  Reported beside value, which stays one stream.
+    streams2 = [torch.cuda.current_stream(), torch.cuda.Stream()]
+    ws2 = [sv.workspace(sv.SV_OP_WINDOW, B, GAMMA, V, torch.bfloat16, dev) for _ in streams2]
+    outs2 = [sv.WindowResult(torch.empty(B, dtype=torch.int32, device=dev),
+                             torch.empty(B, GAMMA + 1, dtype=torch.int32, device=dev)) for _ in streams2]
+
+    def step2(k):
+        i = k & 1
+        d = data[k % len(ALPHAS)]
+        with torch.cuda.stream(streams2[i]):
+            sv.verify_window(d["target"], d["draft"], d["tokens"], seed=0, ws=ws2[i], out=outs2[i])
+
+    for k in range(args.warmup):
+        step2(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step2(k)
+    torch.cuda.synchronize()
+    ms2 = (time.perf_counter() - t0) * 1e3 / args.steps
+    del ws2, outs2
+
     # dominant kernel alone: row statistics, HIP events on its stream
     reps = max(len(ALPHAS), args.steps)
     rs_ms = event_time_ms(torch, lambda it=iter(range(10 ** 9)): step(next(it), sv.api.SV_PART_ROW_STATS), reps)
@@ -204,6 +238,8 @@ def main():
             "bytes_per_launch": alg_bytes,
             "frac_of_probe_read": rs_gbps / probe_gbps,
         },
+        "two_stream_pipelined": {"ms_per_step": ms2, "verified_drafts_per_s": B * GAMMA / (ms2 * 1e-3)},
+        "context_pages": CONTEXT_PAGES,
         "breakdown_us": {"row_stats": rs_ms * 1e3, "decide_sample": ds_ms * 1e3,
                          "full_call_events": full_ms * 1e3},
         "probe_read_GBps": probe_gbps,
@@ -333,6 +369,23 @@ def side_workloads(torch, sv, synth, dev):
         ms = event_time_ms(torch, lambda: sv.verify_window(d["target"], d["draft"], d["tokens"], ws=w), reps)
         nbytes = Bx * (2 * g + 1) * d["V"] * d["target"].element_size()
         out[name] = {"us": ms * 1e3, "GBps": nbytes / (ms * 1e-3) / 1e9}
+
+    # the B=8 window captured once in a HIP graph and replayed (launch-bound)
+    d = synth.window_batch(8, 8, 128256, "bf16", 3.0, 6.0, 1.0, seed=1002, device=dev)
+    w = sv.workspace(sv.SV_OP_WINDOW, 8, 8, 128256, torch.bfloat16, dev)
+    o = sv.WindowResult(torch.empty(8, dtype=torch.int32, device=dev),
+                        torch.empty(8, 9, dtype=torch.int32, device=dev))
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        sv.verify_window(d["target"], d["draft"], d["tokens"], ws=w, out=o)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cs):
+        sv.verify_window(d["target"], d["draft"], d["tokens"], ws=w, out=o)
+    torch.cuda.synchronize()
+    out["window_B8_g8_V128256_bf16_graph_replay"] = {"us": event_time_ms(torch, graph.replay, reps) * 1e3}
+    del graph, d, w, o
 
     # tree (4, 3, 2), B=4, V=50257 fp16
     d = synth.tree_config3(device=dev)
