@@ -28,10 +28,16 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 #ifndef SV_LM_BK
 #define SV_LM_BK 64
 #endif
-constexpr int kBM = SV_LM_BM;              // rows per block: kBM / 64 waves along M
+#ifndef SV_LM_WAVEM
+#define SV_LM_WAVEM 64
+#endif
+constexpr int kBM = SV_LM_BM;              // rows per block
 constexpr int kBN = kLmBN;                 // 2 waves along V, 128 columns each
 constexpr int kBK = SV_LM_BK;
-constexpr int kGemmThreads = 2 * kBM;
+constexpr int kWaveM = SV_LM_WAVEM;        // rows per wave: kBM / kWaveM waves along M
+constexpr int kMT = kWaveM / 32;           // 32-row accumulator tiles per wave
+constexpr int kWavesM = kBM / kWaveM;
+constexpr int kGemmThreads = 64 * kWavesM * 2;
 constexpr int kChunksK = kBK / 8;          // 16-byte chunks per row and K step
 constexpr int kLoadsA = kBM * kChunksK / kGemmThreads;
 constexpr int kLoadsW = kBN * kChunksK / kGemmThreads;
@@ -52,7 +58,7 @@ __device__ __forceinline__ bool lm_tile(int L, int RB, int NT, int *rb, int *ct)
 }
 
 template <int kMode>
-__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(kGemmThreads / 256)))
 k_lm_gemm(LmGemmArgs P) {
   __shared__ uint4 lds_raw[2 * kStageElems * sizeof(uint16_t) / sizeof(uint4)];
   uint16_t *lds = reinterpret_cast<uint16_t *>(lds_raw);
@@ -62,7 +68,7 @@ k_lm_gemm(LmGemmArgs P) {
   if (!lm_tile(blockIdx.x, P.RB, P.NT, &rb, &ct)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % (kBM / 64), wn = wave / (kBM / 64);
+  const int wm = wave % kWavesM, wn = wave / kWavesM;
   const int half = lane >> 5, c32 = lane & 31;
   const int row0 = rb * kBM, col0 = ct * kBN;
 
@@ -96,9 +102,9 @@ k_lm_gemm(LmGemmArgs P) {
     s_tok[tid] = x;
   }
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[kMT][4];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -128,14 +134,14 @@ k_lm_gemm(LmGemmArgs P) {
     if (kt + 1 < nk) {
       SV_LM_FETCH((kt + 1) * kBK)
     }
-    const uint16_t *sa = lds + st * kStageElems + (wm * 64 + c32) * kLdsRow + 8 * half;
+    const uint16_t *sa = lds + st * kStageElems + (wm * kWaveM + c32) * kLdsRow + 8 * half;
     const uint16_t *sw = lds + st * kStageElems + kBM * kLdsRow + (wn * 128 + c32) * kLdsRow + 8 * half;
 #if SV_LM_PIPE
     // operands of K sub-step ks + 1 are read while sub-step ks multiplies; the
     // next tile goes to the other LDS stage in the middle of the step
-    bf16x8_t a[2][2], w[2][4];
+    bf16x8_t a[2][kMT], w[2][4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) a[0][mt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sa + mt * 32 * kLdsRow));
+    for (int mt = 0; mt < kMT; ++mt) a[0][mt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sa + mt * 32 * kLdsRow));
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) w[0][nt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sw + nt * 32 * kLdsRow));
 #pragma unroll
@@ -143,14 +149,14 @@ k_lm_gemm(LmGemmArgs P) {
       const int cur = ks & 1, nxt = cur ^ 1;
       if (ks + 1 < kBK / 16) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < kMT; ++mt)
           a[nxt][mt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sa + mt * 32 * kLdsRow + (ks + 1) * 16));
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
           w[nxt][nt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sw + nt * 32 * kLdsRow + (ks + 1) * 16));
       }
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mt], w[cur][nt], acc[mt][nt], 0, 0, 0);
@@ -161,15 +167,15 @@ k_lm_gemm(LmGemmArgs P) {
 #else
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8_t a[2], w[4];
+      bf16x8_t a[kMT], w[4];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < kMT; ++mt)
         a[mt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sa + mt * 32 * kLdsRow + ks * 16));
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
         w[nt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sw + nt * 32 * kLdsRow + ks * 16));
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], w[nt], acc[mt][nt], 0, 0, 0);
@@ -185,10 +191,10 @@ k_lm_gemm(LmGemmArgs P) {
 
   if (kMode == LM_STORE) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int g = row0 + wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int g = row0 + wm * kWaveM + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
         if (g >= P.M) continue;
         float *orow = P.out + static_cast<int64_t>(g) * P.V;
 #pragma unroll
@@ -205,10 +211,10 @@ k_lm_gemm(LmGemmArgs P) {
   // the 32 lanes of each half-wave; the draft token's logit is picked up by
   // the lane holding its column.
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int rl = wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      const int rl = wm * kWaveM + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
       float v[4];
       float m = kNegInf;
 #pragma unroll
