@@ -1,0 +1,52 @@
+"""Seeded random sweep of window configurations against the oracle: batch,
+window, vocabulary (including sizes that leave rows off 16-byte boundaries),
+dtype, sequence strides, partial windows, sequence ids and base positions,
+each through sv_verify_window, sv_verify_window_early_exit (which must equal
+the full window bit for bit) and sv_verify_greedy (bit-exact).  Margin cases
+are counted; the sweep allows at most one per configuration."""
+import numpy as np
+import pytest
+import torch
+
+import draft_token_verification_06_amd as sv
+from draft_token_verification_06_amd import synth
+from gpu_common import check_greedy, check_window
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _config(k):
+    rng = np.random.default_rng(9000 + k)
+    B = int(rng.choice([1, 3, 8, 33, 130, 300]))
+    gamma = int(rng.choice([1, 2, 5, 8, 17, 64]))
+    V = int(rng.choice([7, 100, 1001, 4097, 32000, 50257]))
+    dtype = str(rng.choice(["bf16", "f16", "f32"]))
+    extra = int(rng.integers(0, 3))  # sequence stride padding, in rows
+    sigma = float(rng.choice([0.2, 1.0, 3.0]))
+    return rng, B, gamma, V, dtype, extra, sigma
+
+
+@pytest.mark.parametrize("k", range(16))
+def test_random_window_configuration(k):
+    rng, B, gamma, V, dtype, extra, sigma = _config(k)
+    if B * (2 * gamma + 1 + 2 * extra) * V > 60_000_000:
+        B = max(1, 60_000_000 // ((2 * gamma + 1 + 2 * extra) * V))
+    print("random config", k, B, gamma, V, dtype, extra, sigma, flush=True)
+    big = synth.window_batch(B, gamma + extra, V, dtype, target_sd=2.5, boost=4.0, sigma=sigma,
+                             seed=700 + k, device=DEV)
+    d = {"target": big["target"][:, : gamma + 1], "draft": big["draft"][:, :gamma],
+         "tokens": big["tokens"][:, :gamma].contiguous(), "dtype": dtype}
+    wl = torch.from_numpy(rng.integers(0, gamma + 1, B).astype(np.int32)).to(DEV)
+    sid = torch.from_numpy(rng.integers(0, 2 ** 40, B).astype(np.int64)).to(DEV)
+    bp = torch.from_numpy(rng.integers(0, 10 ** 6, B).astype(np.int64)).to(DEV)
+    seed, tag = int(rng.integers(0, 2 ** 63)), int(rng.integers(0, 2 ** 32))
+    full = sv.verify_window(d["target"], d["draft"], d["tokens"], seed=seed, tag=tag, window_len=wl,
+                            seq_ids=sid, base_pos=bp, return_probs=True)
+    n, m = check_window(d, full, seed=seed, tag=tag, window_len=wl, seq_ids=sid, base_pos=bp)
+    assert m <= 1
+    ee = sv.verify_window(d["target"], d["draft"], d["tokens"], seed=seed, tag=tag, window_len=wl,
+                          seq_ids=sid, base_pos=bp, return_probs=True, early_exit=True)
+    assert torch.equal(ee.n_accepted, full.n_accepted) and torch.equal(ee.out_tokens, full.out_tokens)
+    g = sv.verify_greedy(d["target"], d["tokens"], window_len=wl)
+    check_greedy(d, g, window_len=wl)
