@@ -48,7 +48,7 @@ KERNEL_SOURCES = ("sv_kernels.hip", "sv_device.h", "sv_plan.h")
 # each scaled by the same counter on the 1 GiB copy this script performs
 # (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000).  Valid for the kernel sources whose
 # hash is recorded; reported as null for any other build.
-PMC_TRAFFIC = {"kernel_sha": "39d3f4b347398268", "bytes": 1117010027}
+PMC_TRAFFIC = {"kernel_sha": "39d3f4b347398268", "bytes": 1117012555}
 
 
 def kernel_sha():
@@ -259,13 +259,16 @@ def main():
 def early_exit_rows(n_accepted, gamma):
     """Rows sv_verify_window_early_exit reads for full windows: every row of
     each position block up to the block holding the sequence's decision
-    (blocks [0,1), [1,3), [3,7), ... over target rows 0..gamma)."""
+    (blocks of doubling width over target rows 0..gamma, the last one taking
+    the rest when at most half a block would remain)."""
     blocks = []
     lo, width = 0, 1
     while lo <= gamma:
         hi = min(gamma + 1, lo + width)
+        if gamma + 1 - hi <= width // 2:
+            hi = gamma + 1
         blocks.append((lo, hi))
-        lo, width = hi, width * 2
+        lo, width = hi, (hi - lo) * 2
     rows = 0
     for n in n_accepted:
         for lo, hi in blocks:

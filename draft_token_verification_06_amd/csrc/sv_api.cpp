@@ -191,11 +191,17 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
     launch_window_finish(dtype, A, B, spart, L.cmax, stream);
     return launch_status();
   }
-  // Position blocks [0,1), [1,3), [3,7), ... up to the bonus row gamma.  A
-  // row workgroup of a sequence that is already done exits at once.
+  // Position blocks of doubling width [0,1), [1,3), [3,7), ... up to the bonus
+  // row gamma; a block that would leave at most half its width behind takes
+  // the rest too (gamma = 8: [0,1), [1,3), [3,9)), which saves a stage's two
+  // launches for a few extra rows.  Blocks stay within one wavefront (<= 48
+  // positions).  A row workgroup of a sequence that is already done exits at
+  // once.
   int32_t *status = reinterpret_cast<int32_t *>(wsb + L.status_off);
   for (int lo = 0, width = 1; lo <= gamma; lo += width, width *= 2) {
-    const int hi = std::min(gamma + 1, lo + width);
+    int hi = std::min(gamma + 1, lo + width);
+    if (gamma + 1 - hi <= width / 2) hi = gamma + 1;
+    width = hi - lo;
     RowSet st = rs;
     st.t0 = st.d0 = lo;
     st.rows_t = hi - lo;

@@ -136,13 +136,15 @@ int sv_verify_window_part(int part, const void *target_logits, int64_t target_se
 
 /* sv_verify_window that stops reading a sequence's rows at its first
  * rejection ("the scan stops at the first rejection"): target and draft rows
- * are reduced in position blocks [0,1), [1,3), [3,7), ..., each followed by a
- * decision; a sequence that has rejected a draft (or used up its window) reads
- * no further rows.  Same arguments and workspace (SV_OP_WINDOW) as
- * sv_verify_window; n_accepted and out_tokens are bit-identical to it, as are
- * p_draft/q_draft for i <= n (they are 0 past n).  The row bytes read shrink
- * from B(2 gamma + 1)V to about B(2 E[n] + 2)V at the cost of 2 launches per
- * block (4 blocks at gamma = 8). */
+ * are reduced in position blocks of doubling width [0,1), [1,3), [3,7), ...,
+ * where a block that would leave at most half its width behind takes the rest
+ * (gamma = 8: [0,1), [1,3), [3,9)), each block followed by a decision; a
+ * sequence that has rejected a draft (or used up its window) reads no further
+ * rows.  Same arguments and workspace (SV_OP_WINDOW) as sv_verify_window;
+ * n_accepted and out_tokens are bit-identical to it, as are p_draft/q_draft
+ * for i <= n (they are 0 past n).  The row bytes read shrink from
+ * B(2 gamma + 1)V to about B(2 E[n] + 2)V at the cost of 2 launches per block
+ * (3 blocks at gamma = 8). */
 int sv_verify_window_early_exit(const void *target_logits, int64_t target_seq_stride,
                                 const void *draft_logits, int64_t draft_seq_stride, int dtype,
                                 const int32_t *draft_tokens, const int32_t *window_len,
