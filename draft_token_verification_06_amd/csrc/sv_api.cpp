@@ -211,9 +211,15 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
     st.status = lo == 0 ? nullptr : status;
     launch_row_stats(dtype, false, st, static_cast<int64_t>(B) * (st.rows_t + st.rows_d) * L.plan.S, part,
                      stream);
-    launch_stage_decide(dtype, A, B, lo, hi, status, stream);
+    if (hi <= gamma) {
+      launch_stage_decide(dtype, A, B, lo, hi, status, stream);
+    } else {  // the last block is decided inside the draw
+      WindowArgs Af = A;
+      Af.stage_lo = lo;
+      Af.status = status;
+      launch_stage_finish(dtype, Af, B, spart, L.cmax, stream);
+    }
   }
-  launch_tree_finish(dtype, jobs, B, V, spart, L.cmax, stream);
   return launch_status();
 }
 

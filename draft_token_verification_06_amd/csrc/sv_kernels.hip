@@ -345,11 +345,12 @@ __device__ void window_decide(const WindowArgs &A, int b, int i, bool write, Sam
 // sequence is done at its first rejection (residual job on that row) or once
 // its window is exhausted (bonus job on row len), and then writes its outputs.
 // Row results, uniforms and the job are the ones sv_verify_window computes.
+// The job goes to *job_out; write_out gates the window outputs, write_status
+// the status word (the last block, decided inside the draw, leaves it alone).
 template <int DT>
-__global__ void __launch_bounds__(kWave) k_stage_decide(WindowArgs A, int lo, int hi, int32_t *__restrict__ status) {
+__device__ __forceinline__ void stage_decide(const WindowArgs &A, int b, int i, int lo, int hi, int32_t *status,
+                                             bool write_out, bool write_status, SampleJob *job_out) {
   using E = Elt<DT>;
-  const int b = blockIdx.x;
-  const int i = threadIdx.x;
   const int p = lo + i;
   const int R = 2 * A.gamma + 1;
   int32_t *out = A.out_tokens + static_cast<int64_t>(b) * (A.gamma + 1);
@@ -360,15 +361,17 @@ __global__ void __launch_bounds__(kWave) k_stage_decide(WindowArgs A, int lo, in
     const bool bad_len = len < 0 || len > A.gamma;
     const bool bad_tok = !bad_len && p < len && (xp < 0 || xp >= A.V);
     if (__any(bad_len || bad_tok)) {
-      for (int k = i; k <= A.gamma; k += kWave) out[k] = -1;
-      for (int k = i; k < A.gamma; k += kWave) {
-        if (A.p_draft) A.p_draft[static_cast<int64_t>(b) * A.gamma + k] = 0.0f;
-        if (A.q_draft) A.q_draft[static_cast<int64_t>(b) * A.gamma + k] = 0.0f;
+      if (write_out) {
+        for (int k = i; k <= A.gamma; k += kWave) out[k] = -1;
+        for (int k = i; k < A.gamma; k += kWave) {
+          if (A.p_draft) A.p_draft[static_cast<int64_t>(b) * A.gamma + k] = 0.0f;
+          if (A.q_draft) A.q_draft[static_cast<int64_t>(b) * A.gamma + k] = 0.0f;
+        }
       }
       if (i == 0) {
-        A.n_accepted[b] = -1;
-        A.jobs[b].mode = JOB_NONE;
-        status[b] = -1;
+        if (write_out) A.n_accepted[b] = -1;
+        job_out->mode = JOB_NONE;
+        if (write_status) status[b] = -1;
       }
       return;
     }
@@ -397,22 +400,24 @@ __global__ void __launch_bounds__(kWave) k_stage_decide(WindowArgs A, int lo, in
   const bool rejected = k < cnt;
   const bool done = rejected || len < hi;
   const int n = rejected ? lo + k : len;  // meaningful when done
-  if (i < cnt && (!done || p <= n)) {
+  if (write_out && i < cnt && (!done || p <= n)) {
     const int64_t o = static_cast<int64_t>(b) * A.gamma + p;
     if (A.p_draft) A.p_draft[o] = P;
     if (A.q_draft) A.q_draft[o] = Q;
   }
   if (!done) {
-    if (i == 0 && lo == 0) status[b] = kSeqVerifying;
+    if (i == 0 && lo == 0 && write_status) status[b] = kSeqVerifying;
     return;
   }
-  for (int q = n + i; q < A.gamma; q += kWave) {  // never examined: past n or past the window
-    if (q == n && n < len) continue;
-    if (A.p_draft) A.p_draft[static_cast<int64_t>(b) * A.gamma + q] = 0.0f;
-    if (A.q_draft) A.q_draft[static_cast<int64_t>(b) * A.gamma + q] = 0.0f;
+  if (write_out) {
+    for (int q = n + i; q < A.gamma; q += kWave) {  // never examined: past n or past the window
+      if (q == n && n < len) continue;
+      if (A.p_draft) A.p_draft[static_cast<int64_t>(b) * A.gamma + q] = 0.0f;
+      if (A.q_draft) A.q_draft[static_cast<int64_t>(b) * A.gamma + q] = 0.0f;
+    }
+    for (int q = i; q <= A.gamma; q += kWave)
+      if (q != n) out[q] = q < n ? A.tokens[static_cast<int64_t>(b) * A.gamma + q] : -1;
   }
-  for (int q = i; q <= A.gamma; q += kWave)
-    if (q != n) out[q] = q < n ? A.tokens[static_cast<int64_t>(b) * A.gamma + q] : -1;
   const int src = (n - lo) & (kWave - 1);
   const MaxSum tn{__shfl(st.m, src), __shfl(st.s, src)};
   const MaxSum dn{__shfl(sd.m, src), __shfl(sd.s, src)};
@@ -433,10 +438,16 @@ __global__ void __launch_bounds__(kWave) k_stage_decide(WindowArgs A, int lo, in
     }
     jb.v = v;
     jb.out_slot = out + n;
-    A.jobs[b] = jb;
-    A.n_accepted[b] = n;
-    status[b] = n;
+    *job_out = jb;
+    if (write_out) A.n_accepted[b] = n;
+    if (write_status) status[b] = n;
   }
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kWave) k_stage_decide(WindowArgs A, int lo, int hi, int32_t *__restrict__ status) {
+  const int b = blockIdx.x;
+  stage_decide<DT>(A, b, threadIdx.x, lo, hi, status, true, true, A.jobs + b);
 }
 
 // ---------------------------------------------------------------------------
@@ -859,29 +870,40 @@ __device__ __forceinline__ int sample_job(const SampleJob &job, int V, float *s_
   return draw_from_sums<DT, false>(job, V, C, 0, s_cs, tid);
 }
 
-// Job of sequence b into s_job: decided here (window, wave 0; writes the
-// window outputs when `write`) or read from the tree decide kernel.
-template <int DT, bool kWindow>
-__device__ __forceinline__ void load_job(const WindowArgs &A, const SampleJob *jobs, int b, bool write,
+// Where the draw's job comes from: the jobs array (tree, or an early-exit
+// sequence decided in an earlier block), the window decision (wave 0), or
+// the early-exit decision of the last position block [A.stage_lo, gamma]
+// (wave 0, for sequences still verifying).  `write` gates the outputs.
+enum : int { SRC_JOBS = 0, SRC_WINDOW = 1, SRC_STAGE = 2 };
+
+// Job of sequence b into s_job; returns whether it was decided here.
+template <int DT, int kSrc>
+__device__ __forceinline__ bool load_job(const WindowArgs &A, const SampleJob *jobs, int b, bool write,
                                          SampleJob *s_job, int tid) {
-  if (kWindow) {
+  bool decided = false;
+  if (kSrc == SRC_WINDOW) {
     if (tid < kWave) window_decide<DT>(A, b, tid, write, s_job);
+    decided = true;
+  } else if (kSrc == SRC_STAGE && A.status[b] == kSeqVerifying) {
+    if (tid < kWave) stage_decide<DT>(A, b, tid, A.stage_lo, A.gamma + 1, A.status, write, false, s_job);
+    decided = true;
   } else if (tid == 0) {
     *s_job = jobs[b];
   }
   __syncthreads();
+  return decided;
 }
 
 // One workgroup per sequence (large batches): decide, one pass over the
 // row(s) with chunk sums in LDS, draw.
-template <int DT, bool kWindow>
+template <int DT, int kSrc>
 __global__ void __launch_bounds__(kFinThreads) k_finish(WindowArgs A, const SampleJob *__restrict__ jobs, int V) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   __shared__ SampleJob s_job;
   __shared__ float s_wp[kFinMaxChunks * kFinWaves];
   __shared__ float s_cs[kFinMaxChunks];
-  load_job<DT, kWindow>(A, jobs, b, true, &s_job, tid);
+  load_job<DT, kSrc>(A, jobs, b, true, &s_job, tid);
   const SampleJob job = s_job;
   if (job.mode == JOB_NONE) return;
   const int y = sample_job<DT>(job, V, s_wp, s_cs, tid);
@@ -891,7 +913,7 @@ __global__ void __launch_bounds__(kFinThreads) k_finish(WindowArgs A, const Samp
 // Small batches, part 1, grid (B, G): workgroup g decides (redundantly, it is
 // cheap) and sums its share of the chunks into spart[b][c]; the g = 0
 // workgroup writes the window outputs and the job.
-template <int DT, bool kWindow>
+template <int DT, int kSrc>
 __global__ void __launch_bounds__(kFinThreads) k_finish_part(WindowArgs A, SampleJob *__restrict__ jobs, int V,
                                                             float *__restrict__ spart, int cmax) {
   const int b = blockIdx.x;
@@ -901,9 +923,9 @@ __global__ void __launch_bounds__(kFinThreads) k_finish_part(WindowArgs A, Sampl
   __shared__ SampleJob s_job;
   __shared__ float s_wp[kFinMaxChunks * kFinWaves];
   __shared__ float s_cs[kFinMaxChunks];
-  load_job<DT, kWindow>(A, jobs, b, g == 0, &s_job, tid);
+  const bool decided = load_job<DT, kSrc>(A, jobs, b, g == 0, &s_job, tid);
   const SampleJob job = s_job;
-  if (kWindow && g == 0 && tid == 0) jobs[b] = job;
+  if (decided && g == 0 && tid == 0) jobs[b] = job;
   if (job.mode == JOB_NONE) return;
   const int h = job_shift(job, Elt<DT>::kBytes);
   const bool vec = h >= 0;
@@ -1214,30 +1236,34 @@ static int finish_split(int B, int V, int dtype) {
   return G < 1 ? 1 : G;
 }
 
-template <int DT, bool kWindow>
+template <int DT, int kSrc>
 static void launch_finish_t(const WindowArgs &A, SampleJob *jobs, int B, int V, float *spart, int cmax,
                             hipStream_t st) {
   const int G = finish_split(B, V, DT);
   if (G == 1) {
-    hipLaunchKernelGGL((k_finish<DT, kWindow>), dim3(B), dim3(kFinThreads), 0, st, A, jobs, V);
+    hipLaunchKernelGGL((k_finish<DT, kSrc>), dim3(B), dim3(kFinThreads), 0, st, A, jobs, V);
   } else {
-    hipLaunchKernelGGL((k_finish_part<DT, kWindow>), dim3(B, G), dim3(kFinThreads), 0, st, A, jobs, V, spart, cmax);
+    hipLaunchKernelGGL((k_finish_part<DT, kSrc>), dim3(B, G), dim3(kFinThreads), 0, st, A, jobs, V, spart, cmax);
     hipLaunchKernelGGL(k_finish_select<DT>, dim3(B), dim3(kFinThreads), 0, st, jobs, V, spart, cmax);
   }
 }
 
-template <bool kWindow>
+template <int kSrc>
 static void launch_finish(int dtype, const WindowArgs &A, SampleJob *jobs, int B, int V, float *spart, int cmax,
                           hipStream_t st) {
   switch (dtype) {
-    case DT_BF16: launch_finish_t<DT_BF16, kWindow>(A, jobs, B, V, spart, cmax, st); break;
-    case DT_F16: launch_finish_t<DT_F16, kWindow>(A, jobs, B, V, spart, cmax, st); break;
-    default: launch_finish_t<DT_F32, kWindow>(A, jobs, B, V, spart, cmax, st); break;
+    case DT_BF16: launch_finish_t<DT_BF16, kSrc>(A, jobs, B, V, spart, cmax, st); break;
+    case DT_F16: launch_finish_t<DT_F16, kSrc>(A, jobs, B, V, spart, cmax, st); break;
+    default: launch_finish_t<DT_F32, kSrc>(A, jobs, B, V, spart, cmax, st); break;
   }
 }
 
 void launch_window_finish(int dtype, const WindowArgs &A, int B, float *spart, int cmax, hipStream_t st) {
-  launch_finish<true>(dtype, A, A.jobs, B, A.V, spart, cmax, st);
+  launch_finish<SRC_WINDOW>(dtype, A, A.jobs, B, A.V, spart, cmax, st);
+}
+
+void launch_stage_finish(int dtype, const WindowArgs &A, int B, float *spart, int cmax, hipStream_t st) {
+  launch_finish<SRC_STAGE>(dtype, A, A.jobs, B, A.V, spart, cmax, st);
 }
 
 void launch_stage_decide(int dtype, const WindowArgs &A, int B, int lo, int hi, int32_t *status, hipStream_t st) {
@@ -1262,7 +1288,7 @@ void launch_tree_decide(int dtype, const TreeArgs &A, int B, hipStream_t st) {
 
 void launch_tree_finish(int dtype, SampleJob *jobs, int B, int V, float *spart, int cmax, hipStream_t st) {
   const WindowArgs none{};
-  launch_finish<false>(dtype, none, jobs, B, V, spart, cmax, st);
+  launch_finish<SRC_JOBS>(dtype, none, jobs, B, V, spart, cmax, st);
 }
 
 void launch_tree_walk(int dtype, const TreeArgs &A, int B, hipStream_t st) {

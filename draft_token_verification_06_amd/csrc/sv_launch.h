@@ -51,6 +51,8 @@ struct WindowArgs {
   int32_t *out_tokens;
   float *p_draft, *q_draft;
   SampleJob *jobs;
+  int32_t stage_lo;   // early exit: first position of the last block (decided in the draw)
+  int32_t *status;    // early exit: per-sequence status
 };
 
 struct GreedyArgs {
@@ -128,6 +130,7 @@ void launch_lm_decide(const LmDecideArgs &A, int B, hipStream_t st);
 void launch_row_stats(int dtype, bool argmax, const RowSet &rs, int64_t blocks, float2 *part, hipStream_t st);
 void launch_window_finish(int dtype, const WindowArgs &A, int B, float *spart, int cmax, hipStream_t st);
 void launch_stage_decide(int dtype, const WindowArgs &A, int B, int lo, int hi, int32_t *status, hipStream_t st);
+void launch_stage_finish(int dtype, const WindowArgs &A, int B, float *spart, int cmax, hipStream_t st);
 void launch_greedy_decide(const GreedyArgs &A, int B, hipStream_t st);
 void launch_tree_decide(int dtype, const TreeArgs &A, int B, hipStream_t st);
 void launch_tree_finish(int dtype, SampleJob *jobs, int B, int V, float *spart, int cmax, hipStream_t st);
