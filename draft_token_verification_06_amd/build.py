@@ -10,8 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspecverify.so")
-SOURCES = [os.path.join(CSRC, "sv_kernels.hip"), os.path.join(CSRC, "sv_lmhead.hip"),
-           os.path.join(CSRC, "sv_api.cpp")]
+SOURCES = [os.path.join(CSRC, "sv_rows.hip"), os.path.join(CSRC, "sv_kernels.hip"),
+           os.path.join(CSRC, "sv_lmhead.hip"), os.path.join(CSRC, "sv_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
