@@ -23,16 +23,39 @@
 
 namespace sv {
 
-// Combine the S segment results of one row, in segment order.
+// Combine the S segment results of one row, in segment order.  The loads go
+// out kSegBatch at a time ahead of their combines, so a row costs
+// ceil(S / kSegBatch) round trips, not S.
+constexpr int kSegBatch = 8;
+
 __device__ __forceinline__ MaxSum row_maxsum(const float2 *p, int S) {
-  MaxSum r{p[0].x, p[0].y};
-  for (int k = 1; k < S; ++k) r = combine(r, MaxSum{p[k].x, p[k].y});
+  MaxSum r{kNegInf, 0.0f};
+  for (int k0 = 0; k0 < S; k0 += kSegBatch) {
+    float2 q[kSegBatch];
+#pragma unroll
+    for (int j = 0; j < kSegBatch; ++j)
+      if (k0 + j < S) q[j] = p[k0 + j];
+#pragma unroll
+    for (int j = 0; j < kSegBatch; ++j)
+      if (k0 + j < S) r = k0 + j == 0 ? MaxSum{q[j].x, q[j].y} : combine(r, MaxSum{q[j].x, q[j].y});
+  }
   return r;
 }
 
 __device__ __forceinline__ MaxIdx row_argmax(const float2 *p, int S) {
-  MaxIdx r{p[0].x, __float_as_int(p[0].y)};
-  for (int k = 1; k < S; ++k) r = combine(r, MaxIdx{p[k].x, __float_as_int(p[k].y)});
+  MaxIdx r{kNegInf, 0};
+  for (int k0 = 0; k0 < S; k0 += kSegBatch) {
+    float2 q[kSegBatch];
+#pragma unroll
+    for (int j = 0; j < kSegBatch; ++j)
+      if (k0 + j < S) q[j] = p[k0 + j];
+#pragma unroll
+    for (int j = 0; j < kSegBatch; ++j)
+      if (k0 + j < S) {
+        const MaxIdx c{q[j].x, __float_as_int(q[j].y)};
+        r = k0 + j == 0 ? c : combine(r, c);
+      }
+  }
   return r;
 }
 

@@ -24,7 +24,9 @@ constexpr int kFinMaxChunks = fin_chunks_max(kMaxVocab);
 constexpr int kFinFillWorkgroups = 256;  // draw workgroups wanted per launch
 constexpr int kMaxSegments = 64;      // row segments (split-row mode)
 constexpr int64_t kFillWorkgroups = 16384;  // row workgroups per launch (256 CUs)
-constexpr int kMinSegment = 4096;     // elements; below this a split does not pay
+// A row splits into at most ceil(V / kMinSegment) segments: shorter segments
+// leave each workgroup too few loads to cover its start-up and reduction.
+constexpr int kMinSegment = 32768;
 
 // Work item of the sampling pass of one sequence: draw from
 //   w_k = p_k                       (BONUS)
@@ -73,7 +75,7 @@ struct RowPlan {
 inline RowPlan plan_rows(int64_t rows_total, int32_t V) {
   int64_t S = 1;
   if (rows_total < kFillWorkgroups) S = (kFillWorkgroups + rows_total - 1) / rows_total;
-  int64_t cap = V / kMinSegment;
+  int64_t cap = (V + kMinSegment - 1) / kMinSegment;
   if (cap < 1) cap = 1;
   if (S > cap) S = cap;
   if (S > kMaxSegments) S = kMaxSegments;

@@ -96,6 +96,20 @@ def test_max_vocabulary():
         sv.verify_window(dd["target"], dd["draft"], dd["tokens"])
 
 
+def test_many_segments_per_row_bf16():
+    """A small batch over a long vocabulary splits each row into 32 segments,
+    so p(x) and q(x) pass through 31 combines of segment results."""
+    V = 1 << 20
+    d = synth.window_batch(2, 8, V, "bf16", target_sd=3.0, boost=6.0, sigma=1.0, seed=20,
+                           device=DEV)
+    res = sv.verify_window(d["target"], d["draft"], d["tokens"], seed=2, return_probs=True)
+    n, m = check_window(d, res, seed=2)
+    assert m <= 1
+    ee = sv.verify_window(d["target"], d["draft"], d["tokens"], seed=2, return_probs=True, early_exit=True)
+    assert torch.equal(ee.n_accepted, res.n_accepted) and torch.equal(ee.out_tokens, res.out_tokens)
+    check_greedy(d, sv.verify_greedy(d["target"], d["tokens"]))
+
+
 @pytest.mark.parametrize("mode", ["greedy", "stochastic"])
 def test_max_tree_256_nodes(mode):
     # 1 + 3 + 9 + 27 + 81 = 121 BFS nodes, then a 135-node chain: 256 nodes, depth 139 > 64
