@@ -595,47 +595,55 @@ __device__ __forceinline__ void chunk_totals(const float *wp, int c_begin, int c
   }
 }
 
-// Inverse CDF from the chunk sums cs[0..C): Z = their sum in chunk order,
-// tau = v * Z, the chunk holding tau, then the first k of that chunk whose
-// running sum exceeds tau (w_k > 0); if rounding leaves none, the chunk's last
-// k with w_k > 0.  cs must be visible to the whole workgroup.
+// Inverse CDF from the chunk sums cs[0..C): wave 0 forms their inclusive
+// prefix sums (a wave scan over 64 chunks at a time, carried in chunk order),
+// Z = the last one, tau = v * Z, and the chunk holding tau is the first whose
+// prefix exceeds it; then the first k of that chunk whose running sum exceeds
+// tau (w_k > 0).  If rounding leaves no such chunk, the last chunk with mass;
+// if it leaves no such k, the chunk's last k with w_k > 0.  cs must be visible
+// to the whole workgroup.
 template <int DT, bool kVec>
 __device__ int draw_from_sums(const SampleJob &job, int V, int C, int h, const float *cs, int tid) {
   using G = FinGeom<DT, kVec>;
   __shared__ float s_base, s_tau;
   __shared__ int s_chunk, s_cand, s_last;
   __shared__ float s_wave_tot[kFinWaves];
-  if (tid == 0) {
-    float Z = 0.0f;
-    for (int c = 0; c < C; ++c) Z += cs[c];
+  __shared__ float s_pref[kFinMaxChunks];
+  if (tid < kWave) {
+    const int lane = tid;
+    float carry = 0.0f;
+    int last_mass = -1;
+    for (int c0 = 0; c0 < C; c0 += kWave) {
+      const int c = c0 + lane;
+      const float x = c < C ? cs[c] : 0.0f;
+      float incl = x;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const float o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      incl += carry;
+      if (c < C) s_pref[c] = incl;
+      const uint64_t mass = __ballot(c < C && x > 0.0f);
+      if (mass) last_mass = c0 + 63 - __builtin_clzll(mass);
+      carry = __shfl(incl, kWave - 1);
+    }
+    const float Z = carry;
     const float tau = job.v * Z;
     int chunk = -1;
-    float run = 0.0f, base = 0.0f;
-    for (int c = 0; c < C; ++c) {
-      const float nxt = run + cs[c];
-      if (nxt > tau) {
-        chunk = c;
-        base = run;
-        break;
-      }
-      run = nxt;
+    for (int c0 = 0; c0 < C && chunk < 0; c0 += kWave) {
+      const int c = c0 + lane;
+      const uint64_t hit = __ballot(c < C && s_pref[c] > tau);
+      if (hit) chunk = c0 + __builtin_ctzll(hit);
     }
-    if (chunk < 0) {  // rounding left tau at or past the total: last chunk with mass
-      run = 0.0f;
-      for (int c = 0; c < C; ++c) {
-        if (cs[c] > 0.0f) {
-          chunk = c;
-          base = run;
-        }
-        run += cs[c];
-      }
-      if (chunk < 0) chunk = 0;
+    if (chunk < 0) chunk = last_mass >= 0 ? last_mass : 0;  // rounding left tau at or past the total
+    if (lane == 0) {
+      s_chunk = chunk;
+      s_base = chunk > 0 ? s_pref[chunk - 1] : 0.0f;
+      s_tau = tau;
+      s_cand = INT_MAX;
+      s_last = -1;
     }
-    s_chunk = chunk;
-    s_base = base;
-    s_tau = tau;
-    s_cand = INT_MAX;
-    s_last = -1;
   }
   __syncthreads();
   const int chunk = s_chunk;
@@ -773,12 +781,15 @@ __global__ void __launch_bounds__(kFinThreads) k_finish_select(const SampleJob *
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   __shared__ float s_cs[kFinMaxChunks];
+  static_assert(kFinMaxChunks <= kFinThreads, "one chunk sum per thread");
+  // the chunk sums travel with the job load (cmax >= C whatever the shift)
+  const float x = tid < cmax ? spart[static_cast<int64_t>(b) * cmax + tid] : 0.0f;
   const SampleJob job = jobs[b];
   if (job.mode == JOB_NONE) return;
   const int h = job_shift(job, Elt<DT>::kBytes);
   const bool vec = h >= 0;
   const int C = vec ? finish_chunks<DT, true>(V, h) : finish_chunks<DT, false>(V, 0);
-  for (int c = tid; c < C; c += kFinThreads) s_cs[c] = spart[static_cast<int64_t>(b) * cmax + c];
+  if (tid < C) s_cs[tid] = x;
   __syncthreads();
   const int y = vec ? draw_from_sums<DT, true>(job, V, C, h, s_cs, tid)
                     : draw_from_sums<DT, false>(job, V, C, 0, s_cs, tid);
