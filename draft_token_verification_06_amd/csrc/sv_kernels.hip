@@ -426,11 +426,16 @@ __global__ void __launch_bounds__(kTreeMaxNodes) k_tree_decide(TreeArgs A) {
 // p_k = 2^(t_k log2e - ct), q_k = 2^(d_k log2e - cd).
 // p_k <= 1 and cq >= 0, so the clamp to [0, 1] is the max (one instruction);
 // with cq = 1 the fused multiply-add rounds exactly like p - q.
-__device__ __forceinline__ float weight_of(const SampleJob &job, float t, float d) {
-  const float p = exp2_fast(__builtin_fmaf(t, kLog2e, -job.ct));
-  if (job.mode != JOB_RESIDUAL) return p;
+__device__ __forceinline__ float bonus_weight(const SampleJob &job, float t) {
+  return exp2_fast(__builtin_fmaf(t, kLog2e, -job.ct));
+}
+__device__ __forceinline__ float residual_weight(const SampleJob &job, float t, float d) {
+  const float p = bonus_weight(job, t);
   const float q = exp2_fast(__builtin_fmaf(d, kLog2e, -job.cd));
   return __builtin_amdgcn_fmed3f(__builtin_fmaf(-job.cq, q, p), 0.0f, 1.0f);
+}
+__device__ __forceinline__ float weight_of(const SampleJob &job, float t, float d) {
+  return job.mode != JOB_RESIDUAL ? bonus_weight(job, t) : residual_weight(job, t, d);
 }
 
 // Geometry of a sampling pass.  Vector geometry (kVec): the row is covered by
@@ -525,14 +530,23 @@ __device__ __forceinline__ void batch_sums(const SampleJob &job, const uint4 *rt
                                            float *wp, int tid) {
   using E = Elt<DT>;
   constexpr int EPV = E::kEPV;
+  // the job is the same for the whole workgroup: one scalar branch here, not
+  // a per-element select between the two weights
+  const bool resid = __builtin_amdgcn_readfirstlane(job.mode) == JOB_RESIDUAL;
 #pragma unroll
   for (int u = 0; u < kFinBatch; ++u) {
-    float xt[EPV], xd[EPV];
+    float xt[EPV];
     E::vec(rt[u], xt);
-    E::vec(rd[u], xd);
     float t = 0.0f;
+    if (resid) {
+      float xd[EPV];
+      E::vec(rd[u], xd);
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) t += weight_of(job, xt[e], xd[e]);
+      for (int e = 0; e < EPV; ++e) t += residual_weight(job, xt[e], xd[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) t += bonus_weight(job, xt[e]);
+    }
     t = wave_sum(t);
     if ((tid & (kWave - 1)) == 0) wp[(c0 + u) * kFinWaves + tid / kWave] = t;
   }
