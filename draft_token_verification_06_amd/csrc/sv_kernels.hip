@@ -369,10 +369,16 @@ __global__ void __launch_bounds__(kTreeMaxNodes) k_tree_decide(TreeArgs A) {
   __syncthreads();
   // A node is accepted when its own test and every ancestor's passed; the
   // deepest accepted node wins, ties to the smallest index (key depth, -index).
-  if (v < N) {
-    bool ok = s_acc[v];
-    for (int u = s_parent[v]; ok && u > 0; u = s_parent[u]) ok = s_acc[u];
-    if (ok) atomicMax(&s_key, (static_cast<int>(A.meta.depth[v]) << 16) | (0xFFFF - v));
+  {
+    int key = -1;
+    if (v < N) {
+      bool ok = s_acc[v];
+      for (int u = s_parent[v]; ok && u > 0; u = s_parent[u]) ok = s_acc[u];
+      if (ok) key = (static_cast<int>(A.meta.depth[v]) << 16) | (0xFFFF - v);
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) key = max(key, __shfl_xor(key, off));
+    if ((v & (kWave - 1)) == 0 && key >= 0) atomicMax(&s_key, key);  // one LDS atomic per wave
   }
   __syncthreads();
   if (v == 0) {
@@ -689,8 +695,13 @@ __device__ int draw_from_sums(const SampleJob &job, int V, int C, int h, const f
     if (cand == INT_MAX && run > tau && w[e] > 0.0f) cand = k0 + e;
     if (w[e] > 0.0f) last = k0 + e;
   }
-  if (cand != INT_MAX) atomicMin(&s_cand, cand);
-  if (last >= 0) atomicMax(&s_last, last);
+  // Slots grow with the thread index, so a wave's first candidate is its
+  // lowest lane with one and its last mass its highest such lane: one LDS
+  // atomic per wave (1024 on one word serialise for microseconds).
+  const uint64_t has_cand = __ballot(cand != INT_MAX);
+  const uint64_t has_last = __ballot(last >= 0);
+  if (has_cand && lane == __builtin_ctzll(has_cand)) atomicMin(&s_cand, cand);
+  if (has_last && lane == 63 - __builtin_clzll(has_last)) atomicMax(&s_last, last);
   __syncthreads();
   int y = s_cand != INT_MAX ? s_cand : s_last;
   if (y < 0) y = max(0, chunk * G::CH - h);  // no mass anywhere: only reachable with invalid logits
