@@ -151,3 +151,37 @@ def test_outputs_are_bitwise_deterministic():
     assert torch.equal(r1.out_tokens, r2.out_tokens)
     assert torch.equal(r1.p_draft.view(torch.int32), r2.p_draft.view(torch.int32))
     assert torch.equal(r1.q_draft.view(torch.int32), r2.q_draft.view(torch.int32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_one_hot_draws_at_slot_wave_and_chunk_boundaries(dtype):
+    """All mass on one token k: the bonus draw (drafts identical to the target)
+    and the residual draw (a draft with all mass elsewhere) must return k, for
+    k at the first and last slot of a thread, of a wave's range and of a
+    chunk, and at the vocabulary's end.  B >= 256 takes the one-workgroup draw,
+    B = 8 the split draw and its select kernel."""
+    V = 3 * 8192 + 517
+    epv = 8 if dtype == "bf16" else 4  # elements per 16-byte slot
+    chunk = 1024 * epv
+    ks = sorted({0, epv - 1, epv, 64 * epv - 1, 64 * epv, chunk - 1, chunk, 2 * chunk + 5, V - 1})
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    for B in (8, 256):
+        gamma = 2
+        k_of = torch.tensor([ks[b % len(ks)] for b in range(B)], device=DEV)
+        t = torch.full((B, gamma + 1, V), -30.0, device=DEV)
+        t[torch.arange(B, device=DEV), :, k_of] = 30.0
+        t = t.to(tdt)
+        # bonus draw: identical draft rows accept every draft token k
+        toks = k_of.to(torch.int32)[:, None].expand(B, gamma).contiguous()
+        res = sv.verify_window(t, t[:, :gamma].contiguous(), toks, seed=11)
+        assert torch.all(res.n_accepted == gamma)
+        assert torch.equal(res.out_tokens[:, gamma].long(), k_of), (dtype, B)
+        # residual draw: the draft puts its mass on j != k and proposes j
+        j_of = (k_of + 1) % V
+        dr = torch.full((B, gamma, V), -30.0, device=DEV)
+        dr[torch.arange(B, device=DEV), :, j_of] = 30.0
+        dr = dr.to(tdt)
+        toks = j_of.to(torch.int32)[:, None].expand(B, gamma).contiguous()
+        res = sv.verify_window(t, dr, toks, seed=12)
+        assert torch.all(res.n_accepted == 0)
+        assert torch.equal(res.out_tokens[:, 0].long(), k_of), (dtype, B)
