@@ -2,15 +2,17 @@
 window, vocabulary (including sizes that leave rows off 16-byte boundaries),
 dtype, sequence strides, partial windows, sequence ids and base positions,
 each through sv_verify_window, sv_verify_window_early_exit (which must equal
-the full window bit for bit) and sv_verify_greedy (bit-exact).  Margin cases
-are counted; the sweep allows at most one per configuration."""
+the full window bit for bit) and sv_verify_greedy (bit-exact).  Then random
+token trees (random parent arrays up to 64 nodes) through sv_verify_tree in
+its three modes.  Margin cases are counted; the sweep allows at most one per
+configuration."""
 import numpy as np
 import pytest
 import torch
 
 import draft_token_verification_06_amd as sv
 from draft_token_verification_06_amd import synth
-from gpu_common import check_greedy, check_window
+from gpu_common import check_greedy, check_tree, check_tree_walk, check_window
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -27,7 +29,7 @@ def _config(k):
     return rng, B, gamma, V, dtype, extra, sigma
 
 
-@pytest.mark.parametrize("k", range(16))
+@pytest.mark.parametrize("k", range(48))
 def test_random_window_configuration(k):
     rng, B, gamma, V, dtype, extra, sigma = _config(k)
     if B * (2 * gamma + 1 + 2 * extra) * V > 60_000_000:
@@ -50,3 +52,25 @@ def test_random_window_configuration(k):
     assert torch.equal(ee.n_accepted, full.n_accepted) and torch.equal(ee.out_tokens, full.out_tokens)
     g = sv.verify_greedy(d["target"], d["tokens"], window_len=wl)
     check_greedy(d, g, window_len=wl)
+
+
+@pytest.mark.parametrize("k", range(24))
+def test_random_tree_configuration(k):
+    rng = np.random.default_rng(7000 + k)
+    N = int(rng.integers(1, 65))
+    # parents within the last few nodes: deep chains and wide levels both occur
+    parent = [-1] + [int(rng.integers(max(0, v - 1 - int(rng.integers(0, 6))), v)) for v in range(1, N)]
+    B = int(rng.choice([1, 3, 8, 32]))
+    V = int(rng.choice([5, 300, 4097, 50257]))
+    dtype = str(rng.choice(["bf16", "f16", "f32"]))
+    sigma = float(rng.choice([0.2, 0.5, 2.0]))
+    print("random tree", k, N, B, V, dtype, sigma, flush=True)
+    d = synth.tree_batch(B, parent, V, dtype=dtype, sigma=sigma, seed=3100 + k, device=DEV)
+    seed = int(rng.integers(0, 2 ** 40))
+    for mode in ("greedy", "stochastic"):
+        res = sv.verify_tree(d["target"], d["draft"], d["tokens"], d["parent"], mode=mode, seed=seed)
+        n, m = check_tree(d, res, mode, seed=seed)
+        assert m <= 1
+    res = sv.verify_tree(d["target"], d["draft"], d["tokens"], d["parent"], mode="multi_candidate", seed=seed)
+    n, m, rej = check_tree_walk(d, res, seed=seed)
+    assert m <= 1
