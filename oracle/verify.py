@@ -17,7 +17,7 @@ Sources (page title, section):
 * Token tree and second speculative stage: "Accelerating LLM Inference with
   Staged Speculative Decoding", abstract.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 * target logits carry gamma+1 rows (the last is the bonus row), draft logits
   gamma rows;
 * the accept test is strict, written u*Q < P (equal to u < min(1, P/Q) since
