@@ -180,9 +180,19 @@ __device__ __forceinline__ void stage_decide(const WindowArgs &A, int b, int i, 
   const int p = lo + i;
   const int R = 2 * A.gamma + 1;
   int32_t *out = A.out_tokens + static_cast<int64_t>(b) * (A.gamma + 1);
-  if (lo > 0 && status[b] != kSeqVerifying) return;
+  // Status, window length, token, ids and this block's row results go out
+  // together (the row results of a finished sequence are stale and unused):
+  // one round trip, then the two logit gathers.
+  const int32_t stat = lo > 0 ? status[b] : kSeqVerifying;
   const int len = A.window_len ? A.window_len[b] : A.gamma;
   const int xp = p < A.gamma ? A.tokens[static_cast<int64_t>(b) * A.gamma + p] : 0;
+  const uint64_t seq = A.seq_ids ? A.seq_ids[b] : static_cast<uint64_t>(b);
+  const int64_t base = A.base_pos ? A.base_pos[b] : 0;
+  const float2 *prow = A.part + static_cast<int64_t>(b) * R * A.S;
+  MaxSum st{0.0f, 1.0f}, sd{0.0f, 1.0f};
+  if (p < hi) st = row_maxsum(prow + p * A.S, A.S);
+  if (p < hi && p < A.gamma) sd = row_maxsum(prow + (A.gamma + 1 + p) * A.S, A.S);
+  if (stat != kSeqVerifying) return;
   if (lo == 0) {
     const bool bad_len = len < 0 || len > A.gamma;
     const bool bad_tok = !bad_len && p < len && (xp < 0 || xp >= A.V);
@@ -202,16 +212,10 @@ __device__ __forceinline__ void stage_decide(const WindowArgs &A, int b, int i, 
       return;
     }
   }
-  const float2 *prow = A.part + static_cast<int64_t>(b) * R * A.S;
   const char *trow0 = A.t + b * A.t_stride_bytes;
   const char *drow0 = A.d + b * A.d_stride_bytes;
   const int64_t row_bytes = static_cast<int64_t>(A.V) * E::kBytes;
-  const uint64_t seq = A.seq_ids ? A.seq_ids[b] : static_cast<uint64_t>(b);
-  const int64_t base = A.base_pos ? A.base_pos[b] : 0;
   const int cnt = min(hi, len) - lo;  // positions examined in this block
-  MaxSum st{0.0f, 1.0f}, sd{0.0f, 1.0f};
-  if (p < hi) st = row_maxsum(prow + p * A.S, A.S);
-  if (p < hi && p < A.gamma) sd = row_maxsum(prow + (A.gamma + 1 + p) * A.S, A.S);
   const U64x4 w = philox4x64_10({seq, static_cast<uint64_t>(base + 1 + p), 0, 0}, A.seed, A.tag);
   const float vi = uniform24(w.c1);
   float P = 0.0f, Q = 0.0f;
