@@ -290,6 +290,10 @@ __global__ void __launch_bounds__(kWave) k_greedy_decide(GreedyArgs A) {
   int32_t *out = A.out_tokens + static_cast<int64_t>(b) * (A.gamma + 1);
   const int len = A.window_len ? A.window_len[b] : A.gamma;
   const int xi = i < A.gamma ? A.tokens[static_cast<int64_t>(b) * A.gamma + i] : 0;
+  // the row results travel with the token loads (rows past the window hold
+  // stale values and are not used)
+  const float2 *prow = A.part + static_cast<int64_t>(b) * R * A.S;
+  const int am_row = i <= A.gamma ? row_argmax(prow + i * A.S, A.S).i : 0;
   const bool bad_len = len < 0 || len > A.gamma;
   const bool bad_tok = !bad_len && i < len && (xi < 0 || xi >= A.V);
   if (__any(bad_len || bad_tok)) {
@@ -298,9 +302,7 @@ __global__ void __launch_bounds__(kWave) k_greedy_decide(GreedyArgs A) {
     return;
   }
   const int x = i < len ? xi : 0;
-  const float2 *prow = A.part + static_cast<int64_t>(b) * R * A.S;
-  int am = 0;
-  if (i <= len) am = row_argmax(prow + i * A.S, A.S).i;
+  const int am = i <= len ? am_row : 0;
   const uint64_t mask = __ballot(i < len && x != am);
   const int n = mask ? __builtin_ctzll(mask) : len;
   int y = __shfl(am, n & (kWave - 1));
@@ -327,6 +329,21 @@ __global__ void __launch_bounds__(kTreeMaxNodes) k_tree_decide(TreeArgs A) {
   int32_t *out_n = A.out_nodes + static_cast<int64_t>(b) * D;
   const int32_t *toks = A.tokens + static_cast<int64_t>(b) * N;
   const int tok = (v >= 1 && v < N) ? toks[v] : 0;
+  // the parent row's results and the ids travel with the token loads
+  const float2 *prow = A.part + static_cast<int64_t>(b) * A.R * A.S;
+  const uint64_t seq = A.seq_ids ? A.seq_ids[b] : static_cast<uint64_t>(b);
+  const int64_t base = A.base_pos ? A.base_pos[b] : 0;
+  int am = -1;
+  MaxSum st{0.0f, 1.0f}, sd{0.0f, 1.0f};
+  if (v >= 1 && v < N) {
+    const int w = A.meta.parent[v];
+    if (A.mode == 0) {
+      am = row_argmax(prow + w * A.S, A.S).i;
+    } else {
+      st = row_maxsum(prow + w * A.S, A.S);
+      sd = row_maxsum(prow + (N + w) * A.S, A.S);
+    }
+  }
   const bool bad = v >= 1 && v < N && (tok < 0 || tok >= A.V);
   if (__syncthreads_or(bad)) {
     for (int k = v; k <= D; k += kTreeMaxNodes) out_t[k] = -1;
@@ -338,12 +355,9 @@ __global__ void __launch_bounds__(kTreeMaxNodes) k_tree_decide(TreeArgs A) {
     }
     return;
   }
-  const float2 *prow = A.part + static_cast<int64_t>(b) * A.R * A.S;
   const int64_t row_bytes = static_cast<int64_t>(A.V) * E::kBytes;
   const char *t0 = A.t + b * A.seq_bytes;
   const char *d0 = A.d ? A.d + b * A.seq_bytes : nullptr;
-  const uint64_t seq = A.seq_ids ? A.seq_ids[b] : static_cast<uint64_t>(b);
-  const int64_t base = A.base_pos ? A.base_pos[b] : 0;
 
   __shared__ unsigned char s_acc[kTreeMaxNodes];
   __shared__ int s_parent[kTreeMaxNodes];
@@ -354,10 +368,8 @@ __global__ void __launch_bounds__(kTreeMaxNodes) k_tree_decide(TreeArgs A) {
     if (v >= 1) {
       const int w = A.meta.parent[v];
       if (A.mode == 0) {
-        acc = tok == row_argmax(prow + w * A.S, A.S).i;
+        acc = tok == am;
       } else {
-        const MaxSum st = row_maxsum(prow + w * A.S, A.S);
-        const MaxSum sd = row_maxsum(prow + (N + w) * A.S, A.S);
         const float P = prob_at(E::one(t0 + w * row_bytes, tok), st);
         const float Q = prob_at(E::one(d0 + w * row_bytes, tok), sd);
         const U64x4 r = philox4x64_10(
