@@ -495,7 +495,6 @@ int sv_verify_window_lmhead(const void *hidden_target, const void *unembed_targe
   G.tokens = draft_tokens;
   G.gamma = gamma;
   G.rows_per_seq = gamma + 1;
-  launch_lm_gemm(LM_STATS, G, stream);
   LmGemmArgs Gd = G;
   Gd.A = static_cast<const uint16_t *>(hidden_draft);
   Gd.lda = Hd;
@@ -505,7 +504,7 @@ int sv_verify_window_lmhead(const void *hidden_target, const void *unembed_targe
   Gd.part = part + Mt * L.NT;
   Gd.gath = gath + Mt;
   Gd.rows_per_seq = gamma;
-  launch_lm_gemm(LM_STATS, Gd, stream);
+  launch_lm_gemm(LM_STATS, G, Gd, stream);
   launch_lm_combine(part, L.NT, static_cast<int>(Mt + Md), stats, stream);
 
   LmDecideArgs D{};
@@ -537,12 +536,11 @@ int sv_verify_window_lmhead(const void *hidden_target, const void *unembed_targe
   S.a_rows = idx;
   S.M = B;
   S.out = rows_t;
-  launch_lm_gemm(LM_STORE, S, stream);
   LmGemmArgs Sd = Gd;
   Sd.a_rows = idx + B;
   Sd.M = B;
   Sd.out = rows_d;
-  launch_lm_gemm(LM_STORE, Sd, stream);
+  launch_lm_gemm(LM_STORE, S, Sd, stream);
 
   launch_tree_finish(SV_DT_F32, jobs, B, V, spart, L.cmax, stream);
   return launch_status();

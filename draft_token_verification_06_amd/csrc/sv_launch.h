@@ -122,7 +122,8 @@ struct LmDecideArgs {
   int32_t *idx_t, *idx_d;        // hidden rows of that pass
 };
 
-void launch_lm_gemm(int mode, LmGemmArgs A, hipStream_t st);
+// Launches the GEMMs of two problems (target rows, draft rows) as one grid.
+void launch_lm_gemm(int mode, LmGemmArgs A0, LmGemmArgs A1, hipStream_t st);
 int lm_gemm_blocks(int M, int V);
 void launch_lm_combine(const float2 *part, int NT, int M, float2 *stats, hipStream_t st);
 void launch_lm_decide(const LmDecideArgs &A, int B, hipStream_t st);

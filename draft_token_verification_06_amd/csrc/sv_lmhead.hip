@@ -57,15 +57,15 @@ __device__ __forceinline__ bool lm_tile(int L, int RB, int NT, int *rb, int *ct)
   return *ct < NT;
 }
 
+// One 256 x 256 output tile of problem P; L is the block's index within P.
 template <int kMode>
-__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(kGemmThreads / 256)))
-k_lm_gemm(LmGemmArgs P) {
+__device__ __forceinline__ void lm_gemm_tile(const LmGemmArgs &P, int L) {
   __shared__ uint4 lds_raw[2 * kStageElems * sizeof(uint16_t) / sizeof(uint4)];
   uint16_t *lds = reinterpret_cast<uint16_t *>(lds_raw);
   __shared__ float2 s_red[2][kBM];
   __shared__ int s_tok[kBM];
   int rb, ct;
-  if (!lm_tile(blockIdx.x, P.RB, P.NT, &rb, &ct)) return;
+  if (!lm_tile(L, P.RB, P.NT, &rb, &ct)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave % kWavesM, wn = wave / kWavesM;
@@ -249,6 +249,20 @@ k_lm_gemm(LmGemmArgs P) {
   }
 }
 
+// Two GEMM problems in one launch (target and draft rows): blocks [0, blocks0)
+// take P0, the rest P1.  One launch fills the tail of the first problem's
+// last round of blocks with the second's.  blocks0 is a multiple of 8, so
+// both problems keep the XCD-aware tile map.
+template <int kMode>
+__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(kGemmThreads / 256)))
+k_lm_gemm(LmGemmArgs P0, LmGemmArgs P1, int blocks0) {
+  const int L = blockIdx.x;
+  if (L < blocks0)
+    lm_gemm_tile<kMode>(P0, L);
+  else
+    lm_gemm_tile<kMode>(P1, L - blocks0);
+}
+
 // Per row, the column-tile partials in a fixed order: lane-strided, then the
 // wave butterfly.  One wave per row.
 __global__ void __launch_bounds__(256) k_lm_combine(const float2 *__restrict__ part, int NT, int M,
@@ -351,14 +365,17 @@ int lm_gemm_blocks(int M, int V) {
   return 8 * ((NT + 7) / 8) * RB;
 }
 
-void launch_lm_gemm(int mode, LmGemmArgs A, hipStream_t st) {
-  A.RB = (A.M + kBM - 1) / kBM;
-  A.NT = (A.V + kBN - 1) / kBN;
-  const int blocks = lm_gemm_blocks(A.M, A.V);
+void launch_lm_gemm(int mode, LmGemmArgs A0, LmGemmArgs A1, hipStream_t st) {
+  A0.RB = (A0.M + kBM - 1) / kBM;
+  A0.NT = (A0.V + kBN - 1) / kBN;
+  A1.RB = (A1.M + kBM - 1) / kBM;
+  A1.NT = (A1.V + kBN - 1) / kBN;
+  const int blocks0 = lm_gemm_blocks(A0.M, A0.V);
+  const int blocks = blocks0 + lm_gemm_blocks(A1.M, A1.V);
   if (mode == LM_STATS)
-    hipLaunchKernelGGL(k_lm_gemm<LM_STATS>, dim3(blocks), dim3(kGemmThreads), 0, st, A);
+    hipLaunchKernelGGL(k_lm_gemm<LM_STATS>, dim3(blocks), dim3(kGemmThreads), 0, st, A0, A1, blocks0);
   else
-    hipLaunchKernelGGL(k_lm_gemm<LM_STORE>, dim3(blocks), dim3(kGemmThreads), 0, st, A);
+    hipLaunchKernelGGL(k_lm_gemm<LM_STORE>, dim3(blocks), dim3(kGemmThreads), 0, st, A0, A1, blocks0);
 }
 
 void launch_lm_combine(const float2 *part, int NT, int M, float2 *stats, hipStream_t st) {
