@@ -95,6 +95,7 @@ def main():
               "(sequences are independent: a batch shards across GPUs with no exchange)",
               file=sys.stderr)
         sys.exit(2)
+    import numpy as np
     import torch
     import draft_token_verification_06_amd as sv
     from draft_token_verification_06_amd import synth
@@ -124,6 +125,9 @@ def main():
     torch.cuda.synchronize()
     ref = [(o.n_accepted.cpu().numpy().copy(), o.out_tokens.cpu().numpy().copy(),
             o.p_draft.cpu().numpy().copy()) for o in outs]
+    # rows the draw re-reads per step, mean over the four batches: the target
+    # and draft rows of the first rejection, or the bonus row after a full window
+    draw_bytes = float(np.mean([sum(2 if n < GAMMA else 1 for n in r[0] if n >= 0) for r in ref])) * V * 2
 
     for k in range(args.warmup):
         step(k)
@@ -224,7 +228,10 @@ def main():
             "frac_of_probe_read": rs_gbps / probe_gbps,
         },
         "two_stream_pipelined": None if ms2 is None else
-        {"ms_per_step": ms2, "verified_drafts_per_s": B * GAMMA / (ms2 * 1e-3)},
+        {"ms_per_step": ms2, "verified_drafts_per_s": B * GAMMA / (ms2 * 1e-3),
+         "GBps_moved": (alg_bytes + draw_bytes) / (ms2 * 1e-3) / 1e9},
+        "draw_bytes_per_step_mean": draw_bytes,
+        "GBps_moved_step": (alg_bytes + draw_bytes) / (ms_per_step * 1e-3) / 1e9,
         "context_pages": CONTEXT_PAGES,
         "breakdown_us": {"row_stats": rs_ms * 1e3, "decide_sample": ds_ms * 1e3,
                          "full_call_events": full_ms * 1e3},
