@@ -9,32 +9,6 @@
 
 namespace sv {
 
-// Rows of one launch of the row-statistics pass.  Sequence b owns rows_t
-// target rows then rows_d draft rows; workgroup (b, j, seg) reduces segment
-// seg of row j.
-// Rows of one launch of the row-statistics pass.  Sequence b owns rows_t
-// target rows (t0, t0+1, ...) then rows_d draft rows (d0, d0+1, ...);
-// workgroup (b, j, seg) reduces segment seg of row j of its sequence and
-// writes part[(b * R_out + slot) * S + seg], slot = t_slot0 + j for target
-// rows and d_slot0 + (j - rows_t) for draft rows.
-struct RowSet {
-  const char *t;
-  int64_t t_stride_bytes;
-  const char *d;
-  int64_t d_stride_bytes;
-  int32_t rows_t, rows_d;
-  int32_t t0, d0;                 // first target / draft row of the launch
-  int32_t R_out, t_slot0, d_slot0;
-  const int32_t *window_len;      // window calls: rows past the window are skipped
-  const int32_t *status;          // early exit: only sequences still verifying
-  int32_t gamma;
-  int32_t V, S, seg_len;
-  uint64_t dmask[kTreeMaxNodes / 64];  // draft row i read iff bit i is set
-};
-
-// Per-sequence state of the early-exit window (workspace): verifying, or done.
-constexpr int32_t kSeqVerifying = -2;
-
 struct WindowArgs {
   const char *t;
   int64_t t_stride_bytes;
@@ -128,7 +102,6 @@ int lm_gemm_blocks(int M, int V);
 void launch_lm_combine(const float2 *part, int NT, int M, float2 *stats, hipStream_t st);
 void launch_lm_decide(const LmDecideArgs &A, int B, hipStream_t st);
 
-void launch_row_stats(int dtype, bool argmax, const RowSet &rs, int64_t blocks, float2 *part, hipStream_t st);
 void launch_window_finish(int dtype, const WindowArgs &A, int B, float *spart, int cmax, hipStream_t st);
 void launch_stage_decide(int dtype, const WindowArgs &A, int B, int lo, int hi, int32_t *status, hipStream_t st);
 void launch_stage_finish(int dtype, const WindowArgs &A, int B, float *spart, int cmax, hipStream_t st);
@@ -137,7 +110,5 @@ void launch_tree_decide(int dtype, const TreeArgs &A, int B, hipStream_t st);
 void launch_tree_finish(int dtype, SampleJob *jobs, int B, int V, float *spart, int cmax, hipStream_t st);
 void launch_tree_walk(int dtype, const TreeArgs &A, int B, hipStream_t st);
 void launch_rollback(const RollbackArgs &A, int S, int stage, hipStream_t st);
-int probe_blocks(size_t bytes);
-void launch_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t st);
 
 }  // namespace sv

@@ -4,9 +4,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "sv_rowset.h"
+
 namespace sv {
 
-constexpr int kRowThreads = 256;      // row-statistics workgroup
 #ifndef SV_FIN_THREADS
 #define SV_FIN_THREADS 1024
 #endif
@@ -50,7 +51,6 @@ struct SampleJob {
 static_assert(sizeof(SampleJob) == 64, "SampleJob is one 64-byte record");
 
 // Tree shape handed to the tree kernels by value.
-constexpr int kTreeMaxNodes = 256;
 constexpr int kTreeMaxDepth = 64;
 struct TreeMeta {
   int32_t N;

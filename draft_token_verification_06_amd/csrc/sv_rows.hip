@@ -9,8 +9,7 @@
 //   step finish the workgroup in a fixed order.
 // k_probe_read: the same nontemporal loads over one contiguous buffer.
 #include "sv_device.h"
-#include "sv_launch.h"
-#include "sv_plan.h"
+#include "sv_rowset.h"
 
 namespace sv {
 
