@@ -150,11 +150,8 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
   rs.t_stride_bytes = target_seq_stride * eb;
   rs.d = static_cast<const char *>(draft_logits);
   rs.d_stride_bytes = draft_seq_stride * eb;
-  rs.rows_t = gamma + 1;
-  rs.rows_d = gamma;
-  rs.t0 = rs.d0 = 0;
+  rs.B = B;
   rs.R_out = 2 * gamma + 1;
-  rs.t_slot0 = 0;
   rs.d_slot0 = gamma + 1;
   rs.window_len = window_len;
   rs.status = nullptr;
@@ -162,7 +159,6 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
   rs.V = V;
   rs.S = L.plan.S;
   rs.seg_len = L.plan.seg_len;
-  for (auto &m : rs.dmask) m = ~0ull;
   WindowArgs A{};
   A.t = rs.t;
   A.t_stride_bytes = rs.t_stride_bytes;
@@ -183,8 +179,12 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
   A.p_draft = p_draft;
   A.q_draft = q_draft;
   A.jobs = jobs;
-  if ((parts & kPartRows) && !(parts & kEarlyExit))
-    launch_row_stats(dtype, false, rs, static_cast<int64_t>(B) * L.rows_per_seq * L.plan.S, part, stream);
+  if ((parts & kPartRows) && !(parts & kEarlyExit)) {
+    RowSet all = rs;
+    all.add_target(0, gamma + 1);
+    all.add_draft(0, gamma);
+    launch_row_stats(dtype, false, all, part, stream);
+  }
   if (!(parts & (kPartFinish | kEarlyExit))) return launch_status();
   float *spart = reinterpret_cast<float *>(wsb + L.spart_off);
   if (!(parts & kEarlyExit)) {
@@ -203,14 +203,10 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
     if (gamma + 1 - hi <= width / 2) hi = gamma + 1;
     width = hi - lo;
     RowSet st = rs;
-    st.t0 = st.d0 = lo;
-    st.rows_t = hi - lo;
-    st.rows_d = std::max(0, std::min(hi, static_cast<int>(gamma)) - lo);
-    st.t_slot0 = lo;
-    st.d_slot0 = gamma + 1 + lo;
+    st.add_target(lo, hi);
+    st.add_draft(lo, std::min(hi, static_cast<int>(gamma)));
     st.status = lo == 0 ? nullptr : status;
-    launch_row_stats(dtype, false, st, static_cast<int64_t>(B) * (st.rows_t + st.rows_d) * L.plan.S, part,
-                     stream);
+    launch_row_stats(dtype, false, st, part, stream);
     if (hi <= gamma) {
       launch_stage_decide(dtype, A, B, lo, hi, status, stream);
     } else {  // the last block is decided inside the draw
@@ -294,11 +290,8 @@ int sv_verify_greedy(const void *target_logits, int64_t target_seq_stride, int d
   rs.t = static_cast<const char *>(target_logits);
   rs.t_stride_bytes = target_seq_stride * eb;
   rs.d = nullptr;
-  rs.rows_t = gamma + 1;
-  rs.rows_d = 0;
-  rs.t0 = rs.d0 = 0;
+  rs.B = B;
   rs.R_out = gamma + 1;
-  rs.t_slot0 = 0;
   rs.d_slot0 = gamma + 1;
   rs.window_len = window_len;
   rs.status = nullptr;
@@ -306,7 +299,8 @@ int sv_verify_greedy(const void *target_logits, int64_t target_seq_stride, int d
   rs.V = V;
   rs.S = L.plan.S;
   rs.seg_len = L.plan.seg_len;
-  launch_row_stats(dtype, true, rs, static_cast<int64_t>(B) * L.rows_per_seq * L.plan.S, part, stream);
+  rs.add_target(0, gamma + 1);
+  launch_row_stats(dtype, true, rs, part, stream);
 
   GreedyArgs A{};
   A.tokens = draft_tokens;
@@ -361,11 +355,8 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
   rs.t_stride_bytes = seq_bytes;
   rs.d = static_cast<const char *>(draft_logits);
   rs.d_stride_bytes = seq_bytes;
-  rs.rows_t = N;
-  rs.rows_d = sampled ? N : 0;
-  rs.t0 = rs.d0 = 0;
+  rs.B = B;
   rs.R_out = 2 * N;
-  rs.t_slot0 = 0;
   rs.d_slot0 = N;
   rs.window_len = nullptr;
   rs.status = nullptr;
@@ -373,18 +364,15 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
   rs.V = V;
   rs.S = L.plan.S;
   rs.seg_len = L.plan.seg_len;
-  for (int k = 0; k < kTreeMaxNodes / 64; ++k) rs.dmask[k] = meta.internal[k];
-  // The plan is laid out for 2N rows per sequence; greedy launches only the
-  // first N of them (target rows) but keeps the same partial-row indexing.
+  // Row results are laid out for 2N rows per sequence (draft row v at slot
+  // N + v); only the rows the decision reads are listed: every target row,
+  // and, when sampling, the draft rows of nodes with children.
+  rs.add_target(0, N);
+  if (sampled)
+    for (int v = 0; v < N; ++v)
+      if ((meta.internal[v >> 6] >> (v & 63)) & 1ull) rs.add_draft(v, v + 1);
+  launch_row_stats(dtype, !sampled, rs, part, stream);
   const int R = 2 * N;
-  if (sampled) {
-    launch_row_stats(dtype, false, rs, static_cast<int64_t>(B) * R * L.plan.S, part, stream);
-  } else {
-    RowSet g = rs;
-    g.rows_d = N;  // keep the 2N-row indexing; draft rows are masked off
-    for (auto &m : g.dmask) m = 0;
-    launch_row_stats(dtype, true, g, static_cast<int64_t>(B) * R * L.plan.S, part, stream);
-  }
 
   TreeArgs A{};
   A.t = rs.t;

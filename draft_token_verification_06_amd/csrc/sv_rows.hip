@@ -170,12 +170,11 @@ __device__ __forceinline__ void stream_segment(const char *row, int lo, int hi, 
 template <int DT, bool kArgmax>
 __global__ void __launch_bounds__(kRowThreads) k_row_stats(RowSet rs, float2 *__restrict__ part) {
   using E = Elt<DT>;
-  const uint32_t R = rs.rows_t + rs.rows_d;
   const uint32_t blk = blockIdx.x;  // B * R * S < 2^31 (checked on the host)
   const int seg = static_cast<int>(blk % static_cast<uint32_t>(rs.S));
   const uint32_t rj = blk / static_cast<uint32_t>(rs.S);
-  const int j = static_cast<int>(rj % R);
-  const int64_t b = rj / R;
+  const int j = static_cast<int>(rj % static_cast<uint32_t>(rs.R));
+  const int64_t b = rj / static_cast<uint32_t>(rs.R);
 
   if (rs.status && rs.status[b] != kSeqVerifying) return;
   int len = rs.gamma;
@@ -183,19 +182,18 @@ __global__ void __launch_bounds__(kRowThreads) k_row_stats(RowSet rs, float2 *__
     len = rs.window_len[b];
     if (len < 0 || len > rs.gamma) return;
   }
+  const int e = rs.row[j];
+  const int i = e & ~kDraftRow;
   const char *row;
   int slot;
-  if (j < rs.rows_t) {
-    const int i = rs.t0 + j;
+  if (!(e & kDraftRow)) {
     if (rs.window_len && i > len) return;
     row = rs.t + b * rs.t_stride_bytes + static_cast<int64_t>(i) * rs.V * E::kBytes;
-    slot = rs.t_slot0 + j;
+    slot = i;
   } else {
-    const int i = rs.d0 + (j - rs.rows_t);
     if (rs.window_len && i >= len) return;
-    if (!((rs.dmask[i >> 6] >> (i & 63)) & 1ull)) return;
     row = rs.d + b * rs.d_stride_bytes + static_cast<int64_t>(i) * rs.V * E::kBytes;
-    slot = rs.d_slot0 + (j - rs.rows_t);
+    slot = rs.d_slot0 + i;
   }
 
   const int lo = seg * rs.seg_len;
@@ -250,7 +248,9 @@ __global__ void __launch_bounds__(kRowThreads) k_probe_read(const uint4 *__restr
 // Launchers (host side)
 // ---------------------------------------------------------------------------
 template <bool kArgmax>
-static void launch_row_stats_t(int dtype, const RowSet &rs, int64_t blocks, float2 *part, hipStream_t st) {
+static void launch_row_stats_t(int dtype, const RowSet &rs, float2 *part, hipStream_t st) {
+  const int64_t blocks = static_cast<int64_t>(rs.B) * rs.R * rs.S;
+  if (blocks < 1) return;
   const dim3 grid(static_cast<unsigned>(blocks)), block(kRowThreads);
   switch (dtype) {
     case DT_BF16: hipLaunchKernelGGL((k_row_stats<DT_BF16, kArgmax>), grid, block, 0, st, rs, part); break;
@@ -259,9 +259,9 @@ static void launch_row_stats_t(int dtype, const RowSet &rs, int64_t blocks, floa
   }
 }
 
-void launch_row_stats(int dtype, bool argmax, const RowSet &rs, int64_t blocks, float2 *part, hipStream_t st) {
-  if (argmax) launch_row_stats_t<true>(dtype, rs, blocks, part, st);
-  else launch_row_stats_t<false>(dtype, rs, blocks, part, st);
+void launch_row_stats(int dtype, bool argmax, const RowSet &rs, float2 *part, hipStream_t st) {
+  if (argmax) launch_row_stats_t<true>(dtype, rs, part, st);
+  else launch_row_stats_t<false>(dtype, rs, part, st);
 }
 
 int probe_blocks(size_t bytes) {
