@@ -15,6 +15,11 @@ namespace {
 
 constexpr int kVersion = 10000;  // 1.0.0
 
+// The row list of a launch holds a full window's rows and a tree's target rows
+// plus its internal draft rows.
+static_assert(kMaxLaunchRows >= 2 * SV_MAX_GAMMA + 1, "row list too short for a window");
+static_assert(kMaxLaunchRows >= 2 * kTreeMaxNodes - 1, "row list too short for a tree");
+
 int elem_bytes(int dtype) {
   switch (dtype) {
     case SV_DT_F32: return 4;
