@@ -64,6 +64,35 @@ def _optional(t, dtype, B, name):
     return t
 
 
+def _same_device(dev, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _ws_bytes(ws, dev):
+    """Byte size of a caller-supplied workspace (a contiguous device tensor)."""
+    if not ws.is_cuda or not ws.is_contiguous() or ws.device != dev:
+        raise ValueError(f"workspace: expected a contiguous device tensor on {dev}")
+    return ws.numel() * ws.element_size()
+
+
+def _out_tensor(t, dtype, shape, dev, name):
+    if t is None:
+        return
+    if t.dtype != dtype or t.device != dev or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected a contiguous {dtype} tensor of shape {tuple(shape)} on {dev}")
+
+
+def _check_window_out(out, B, gamma, dev):
+    if out.n_accepted is None or out.out_tokens is None:
+        raise ValueError("n_accepted and out_tokens are required outputs")
+    _out_tensor(out.n_accepted, torch.int32, (B,), dev, "n_accepted")
+    _out_tensor(out.out_tokens, torch.int32, (B, gamma + 1), dev, "out_tokens")
+    _out_tensor(out.p_draft, torch.float32, (B, gamma), dev, "p_draft")
+    _out_tensor(out.q_draft, torch.float32, (B, gamma), dev, "q_draft")
+
+
 def workspace_size(op, B, n, V, dtype):
     return int(lib().sv_workspace_size(op, B, n, V, _DTYPE_CODE[dtype]))
 
@@ -110,14 +139,21 @@ def verify_window(target, draft, tokens, *, seed=0, tag=0, window_len=None, seq_
     _optional(seq_ids, torch.int64, B, "seq_ids")
     _optional(base_pos, torch.int64, B, "base_pos")
     dev = target.device
+    _same_device(dev, draft=draft, tokens=tokens, window_len=window_len, seq_ids=seq_ids,
+                 base_pos=base_pos)
     if ws is None:
         ws = workspace(SV_OP_WINDOW, B, gamma, V, target.dtype, dev)
+        ws_bytes = ws.numel()
+    else:
+        ws_bytes = _ws_bytes(ws, dev)
     if out is None:
         out = WindowResult(torch.empty(B, dtype=torch.int32, device=dev),
                            torch.empty(B, gamma + 1, dtype=torch.int32, device=dev))
         if return_probs:
             out.p_draft = torch.empty(B, gamma, dtype=torch.float32, device=dev)
             out.q_draft = torch.empty(B, gamma, dtype=torch.float32, device=dev)
+    else:
+        _check_window_out(out, B, gamma, dev)
     if early_exit:
         if part is not None:
             raise ValueError("early_exit has no parts")
@@ -130,7 +166,7 @@ def verify_window(target, draft, tokens, *, seed=0, tag=0, window_len=None, seq_
             _ptr(tokens), _ptr(window_len), B, gamma, V,
             ctypes.c_uint64(seed), ctypes.c_uint64(tag), _ptr(seq_ids), _ptr(base_pos),
             _ptr(out.n_accepted), _ptr(out.out_tokens), _ptr(out.p_draft), _ptr(out.q_draft),
-            _ptr(ws), ws.numel(), _stream(dev)))
+            _ptr(ws), ws_bytes, _stream(dev)))
     return out
 
 
@@ -154,8 +190,13 @@ def verify_window_lmhead(h_target, w_target, h_draft, w_draft, tokens, *, seed=0
     _optional(seq_ids, torch.int64, B, "seq_ids")
     _optional(base_pos, torch.int64, B, "base_pos")
     dev = h_target.device
+    _same_device(dev, w_target=w_target, h_draft=h_draft, w_draft=w_draft, tokens=tokens,
+                 window_len=window_len, seq_ids=seq_ids, base_pos=base_pos)
     if ws is None:
         ws = workspace(SV_OP_LMHEAD, B, gamma, V, torch.bfloat16, dev)
+        ws_bytes = ws.numel()
+    else:
+        ws_bytes = _ws_bytes(ws, dev)
     out = WindowResult(torch.empty(B, dtype=torch.int32, device=dev),
                        torch.empty(B, gamma + 1, dtype=torch.int32, device=dev))
     if return_probs:
@@ -167,7 +208,7 @@ def verify_window_lmhead(h_target, w_target, h_draft, w_draft, tokens, *, seed=0
             _ptr(tokens), _ptr(window_len), B, gamma, V,
             ctypes.c_uint64(seed), ctypes.c_uint64(tag), _ptr(seq_ids), _ptr(base_pos),
             _ptr(out.n_accepted), _ptr(out.out_tokens), _ptr(out.p_draft), _ptr(out.q_draft),
-            _ptr(ws), ws.numel(), _stream(dev)))
+            _ptr(ws), ws_bytes, _stream(dev)))
     return out
 
 
@@ -179,16 +220,25 @@ def verify_greedy(target, tokens, *, window_len=None, ws=None, out=None):
     _i32(tokens, (B, gamma), "tokens")
     _optional(window_len, torch.int32, B, "window_len")
     dev = target.device
+    _same_device(dev, tokens=tokens, window_len=window_len)
     if ws is None:
         ws = workspace(SV_OP_GREEDY, B, gamma, V, target.dtype, dev)
+        ws_bytes = ws.numel()
+    else:
+        ws_bytes = _ws_bytes(ws, dev)
     if out is None:
         out = WindowResult(torch.empty(B, dtype=torch.int32, device=dev),
                            torch.empty(B, gamma + 1, dtype=torch.int32, device=dev))
+    else:
+        if out.n_accepted is None or out.out_tokens is None:
+            raise ValueError("n_accepted and out_tokens are required outputs")
+        _out_tensor(out.n_accepted, torch.int32, (B,), dev, "n_accepted")
+        _out_tensor(out.out_tokens, torch.int32, (B, gamma + 1), dev, "out_tokens")
     with torch.cuda.device(dev):
         _check(lib().sv_verify_greedy(
             _ptr(target), ts, _DTYPE_CODE[target.dtype], _ptr(tokens), _ptr(window_len),
             B, gamma, V, _ptr(out.n_accepted), _ptr(out.out_tokens),
-            _ptr(ws), ws.numel(), _stream(dev)))
+            _ptr(ws), ws_bytes, _stream(dev)))
     return out
 
 
@@ -222,8 +272,15 @@ def verify_tree(target, draft, node_tokens, parent, *, mode="stochastic", seed=0
     _optional(base_pos, torch.int64, B, "base_pos")
     D = tree_max_depth(parent)
     dev = target.device
+    if not target.is_cuda or target.dtype not in _DTYPE_CODE:
+        raise ValueError("target: expected float32, bfloat16 or float16 device logits")
+    _same_device(dev, draft=draft if sampled else None, node_tokens=node_tokens, seq_ids=seq_ids,
+                 base_pos=base_pos)
     if ws is None:
         ws = workspace(SV_OP_TREE, B, N, V, target.dtype, dev)
+        ws_bytes = ws.numel()
+    else:
+        ws_bytes = _ws_bytes(ws, dev)
     res = TreeResult(torch.empty(B, dtype=torch.int32, device=dev),
                      torch.empty(B, dtype=torch.int32, device=dev),
                      torch.empty(B, D + 1, dtype=torch.int32, device=dev),
@@ -235,12 +292,14 @@ def verify_tree(target, draft, node_tokens, parent, *, mode="stochastic", seed=0
             _DTYPE_CODE[target.dtype], _ptr(node_tokens), par, B, N, V, code,
             ctypes.c_uint64(seed), ctypes.c_uint64(tag), _ptr(seq_ids), _ptr(base_pos),
             _ptr(res.n_accepted), _ptr(res.best_node), _ptr(res.out_tokens), _ptr(res.out_nodes),
-            _ptr(ws), ws.numel(), _stream(dev)))
+            _ptr(ws), ws_bytes, _stream(dev)))
     return res
 
 
 def rollback(buf_tokens, buf_len, stage, verified, verified_len, *, len_offset=0):
-    """Per-stage buffer rollback: sv_rollback (in place on buf_tokens/buf_len)."""
+    """Per-stage buffer rollback: sv_rollback (in place on buf_tokens/buf_len).
+    Row s of `verified` must hold at least verified_len[s] + len_offset tokens
+    (at most cap are read); that length lives on the device and is not checked here."""
     S, K, cap = buf_tokens.shape
     _i32(buf_tokens, (S, K, cap), "buf_tokens")
     _i32(buf_len, (S, K), "buf_len")
@@ -249,6 +308,7 @@ def rollback(buf_tokens, buf_len, stage, verified, verified_len, *, len_offset=0
         raise ValueError("verified: expected an int32 device tensor (S, >=L) with unit column stride")
     _i32(verified_len, (S,), "verified_len")
     dev = buf_tokens.device
+    _same_device(dev, buf_len=buf_len, verified=verified, verified_len=verified_len)
     with torch.cuda.device(dev):
         _check(lib().sv_rollback(
             _ptr(buf_tokens), _ptr(buf_len), S, K, cap, stage,

@@ -217,7 +217,10 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
  *   verified_tokens: stream s's verified sequence starts at
  *                 verified_tokens + s * verified_stride (int32 elements);
  *   verified_len [S]: its length is verified_len[s] + len_offset
- *                 (len_offset = 1 lets n_accepted of a verify call be passed).
+ *                 (len_offset = 1 lets n_accepted of a verify call be passed);
+ *                 the caller provides at least that many tokens per sequence
+ *                 (a length in [0, cap] is read; the library cannot check the
+ *                 width of the verified rows).
  *   stage in [1, K-1]: buffers 0..stage-1 are rolled back, others untouched.
  * For each j < stage with L the verified length: m = first t < min(len_j, L)
  * where buffer j differs from the verified sequence, else min(len_j, L); if

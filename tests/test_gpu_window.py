@@ -185,3 +185,42 @@ def test_one_hot_draws_at_slot_wave_and_chunk_boundaries(dtype):
         res = sv.verify_window(t, dr, toks, seed=12)
         assert torch.all(res.n_accepted == 0)
         assert torch.equal(res.out_tokens[:, 0].long(), k_of), (dtype, B)
+
+
+def test_binding_rejects_malformed_outputs_and_workspaces():
+    B, gamma, V = 4, 3, 64
+    d = synth.window_batch(B, gamma, V, "bf16", sigma=0.5, seed=2, device=DEV)
+    good = sv.WindowResult(torch.empty(B, dtype=torch.int32, device=DEV),
+                           torch.empty(B, gamma + 1, dtype=torch.int32, device=DEV))
+    bad_outputs = [
+        sv.WindowResult(torch.empty(B, dtype=torch.int32, device=DEV),
+                        torch.empty(B, gamma, dtype=torch.int32, device=DEV)),        # too narrow
+        sv.WindowResult(torch.empty(B + 1, dtype=torch.int32, device=DEV),
+                        torch.empty(B, gamma + 1, dtype=torch.int32, device=DEV)),    # wrong batch
+        sv.WindowResult(torch.empty(B, dtype=torch.int64, device=DEV),
+                        torch.empty(B, gamma + 1, dtype=torch.int32, device=DEV)),    # wrong dtype
+        sv.WindowResult(torch.empty(B, dtype=torch.int32),
+                        torch.empty(B, gamma + 1, dtype=torch.int32)),                # host memory
+        sv.WindowResult(torch.empty(B, dtype=torch.int32, device=DEV),
+                        torch.empty(gamma + 1, B, dtype=torch.int32, device=DEV).t()),  # not contiguous
+        sv.WindowResult(good.n_accepted, good.out_tokens,
+                        torch.empty(B, gamma - 1, dtype=torch.float32, device=DEV)),  # p_draft too narrow
+    ]
+    for out in bad_outputs:
+        with pytest.raises(ValueError):
+            sv.verify_window(d["target"], d["draft"], d["tokens"], out=out)
+    for out in bad_outputs[:5]:
+        with pytest.raises(ValueError):
+            sv.verify_greedy(d["target"], d["tokens"], out=out)
+    ws = sv.workspace(sv.SV_OP_WINDOW, B, gamma, V, torch.bfloat16, DEV)
+    with pytest.raises(ValueError):
+        sv.verify_window(d["target"], d["draft"], d["tokens"], ws=ws.cpu())
+    with pytest.raises(ValueError):
+        sv.verify_window(d["target"], d["draft"], d["tokens"], ws=ws.view(-1, 2).t())
+    with pytest.raises(ValueError):
+        sv.verify_window(d["target"], d["draft"], d["tokens"].cpu())
+    # a workspace of another dtype counts in bytes
+    r = sv.verify_window(d["target"], d["draft"], d["tokens"], ws=ws.view(torch.int32), out=good)
+    ref = sv.verify_window(d["target"], d["draft"], d["tokens"])
+    torch.cuda.synchronize()
+    assert torch.equal(r.n_accepted, ref.n_accepted) and torch.equal(r.out_tokens, ref.out_tokens)
