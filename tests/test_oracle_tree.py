@@ -8,6 +8,9 @@
   first emitted token (brute force over the uniform grid) equals
   (1 - alpha) p + min(p, q), the closed form of the per-node acceptance
   reading; with one child it reduces to p.
+* Branching (2, 2): per-node pass thresholds against the parent's rows, the end
+  node of every accept pattern (deepest, smallest index) and the emitted
+  token's law, against an independent enumeration.
 """
 
 import numpy as np
@@ -143,3 +146,80 @@ def test_depth_one_tree_exact_first_token_law(children):
             law += w * reject_all * res
     want = (1 - alpha) * p + np.minimum(p, q) if children == 2 else p
     assert np.allclose(law, want, atol=8 * V / GRID)
+
+
+@pytest.mark.parametrize("tie_tokens", [False, True])
+def test_branching_tree_exact_output_law(tie_tokens):
+    """Branching (2, 2), V = 5: every accept pattern of the six non-root nodes.
+
+    Independently of the oracle (scipy's softmax, plain loops): node v passes
+    with probability a_v = min(1, p_w(x_v) / q_w(x_v)) against its parent w's
+    rows; on a pattern of passes the path ends at the deepest node whose whole
+    chain passed (smallest index among equals); the emitted token follows the
+    renormalised max(0, p_d - q_d) when d has children, else p_d.  The oracle
+    must give, on the 2^-24 uniform grid: each node's pass threshold a_v, the
+    same end node d for every pattern, and that token law (bisection on v)."""
+    from scipy.special import softmax as sp_softmax
+
+    rng = np.random.default_rng(91 + tie_tokens)
+    V = 5
+    parent = bfs_tree((2, 2))
+    N = len(parent)
+    T = rng.normal(0, 1, (N, V))
+    D = T + rng.normal(0, 0.8, (N, V))
+    P = [sp_softmax(T[w]) for w in range(N)]
+    Q = [sp_softmax(D[w]) for w in range(N)]
+    # every node but 2 carries the token with the smallest p/q under its parent,
+    # so it can fail and each internal node can end the path; node 2 carries a
+    # draft sample (it may be one that always passes)
+    toks = [0] + [int(np.argmin(P[parent[v]] / Q[parent[v]])) for v in range(1, N)]
+    toks[2] = int(rng.choice(V, p=Q[0]))
+    if tie_tokens:          # siblings carry the same token, so their tests differ only by u
+        toks[2] = toks[1]
+        toks[4] = toks[3]
+    a = [1.0] + [min(1.0, P[parent[v]][toks[v]] / Q[parent[v]][toks[v]]) for v in range(1, N)]
+    depth = [0] * N
+    for v in range(1, N):
+        depth[v] = depth[parent[v]] + 1
+    has_child = [any(parent[c] == v for c in range(N)) for v in range(N)]
+
+    def run(us, vv):
+        return verify_tree(T, D, toks, parent, "stochastic", [0.0] + list(us), [vv] * N)
+
+    # per-node pass threshold: node v alone varies, every other node passes
+    for v in range(1, N):
+        def passes(k, v=v):
+            us = [0.0] * (N - 1)
+            us[v - 1] = k / GRID
+            return run(us, 0.0)["ok"][v]
+        assert abs(_count_true(passes) / GRID - a[v]) <= 2.0 / GRID, v
+
+    ends = set()
+    for pattern in range(1 << (N - 1)):
+        bits = [True] + [bool((pattern >> (v - 1)) & 1) for v in range(1, N)]
+        if any(not bits[v] and a[v] >= UMAX for v in range(1, N)):
+            continue  # a node that cannot fail
+        ok = [True] * N
+        for v in range(1, N):
+            ok[v] = ok[parent[v]] and bits[v]
+        d = 0
+        for v in range(N):
+            if ok[v] and depth[v] > depth[d]:
+                d = v
+        if has_child[d]:
+            w = np.maximum(0.0, P[d] - Q[d])
+            w = w / w.sum()
+        else:
+            w = P[d]
+        us = [0.0 if bits[v] else UMAX for v in range(1, N)]
+        r = run(us, 0.0)
+        assert r["best"] == d and r["ok"] == ok, (pattern, r["best"], d)
+        law = np.zeros(V)
+        prev = 0
+        for t in range(V):
+            nxt = _count_true(lambda k: run(us, k / GRID)["out"][-1] <= t)
+            law[t] = (nxt - prev) / GRID
+            prev = nxt
+        assert np.allclose(law, w, atol=2.0 / GRID), (pattern, law, w)
+        ends.add(d)
+    assert {1, 2} <= ends and ends & {3, 4, 5, 6}  # residual draws at both depths and bonus draws
