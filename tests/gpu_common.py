@@ -17,6 +17,15 @@ MARGIN = 1e-5
 PROB_RTOL = 1e-5
 
 
+def max_margins(n_sequences):
+    """Margin cases to allow among n sequences.  The GPU forms ratios and CDFs
+    in float32, so a draw whose tau lies within about 1e-6 of a CDF boundary
+    (relative to the total) can land on the other side; on flat rows of
+    32000 tokens that is 1-2% of draws.  Every counted case is still checked
+    to be a margin case; this only bounds how many there may be."""
+    return 1 + n_sequences // 50
+
+
 def host_rows(t, dtype):
     return oracle.decode(to_host_bits(t), dtype)
 
@@ -71,7 +80,7 @@ def check_window(data, res, *, seed, tag=0, window_len=None, seq_ids=None, base_
         if ng != o["n"]:
             assert _decision_margin(o, min(ng, o["n"])), (b, ng, o["n"], list(out_gpu[b]), o["out"])
         else:
-            assert list(out_gpu[b][:ng]) == o["out"][:ng]
+            assert list(out_gpu[b][:ng]) == o["out"][:ng], (b, list(out_gpu[b]), o["out"])
             assert _sample_margin(o["sample"]), (b, list(out_gpu[b]), o["out"], o["sample"])
         margins += 1
     return len(rows), margins
@@ -245,7 +254,7 @@ def check_lmhead(data, res, *, seed, tag=0, window_len=None, rows=None):
                        for i, r in enumerate(o["ratio"][: min(ng, o["n"]) + 1]))
             assert near, (b, ng, o["n"], list(out_gpu[b]), o["out"])
         else:
-            assert list(out_gpu[b][:ng]) == o["out"][:ng]
+            assert list(out_gpu[b][:ng]) == o["out"][:ng], (b, list(out_gpu[b]), o["out"])
             s = o["sample"]
             tol = MARGIN + 2 * (tp + tq)
             assert abs(s["tau"] - s["C_lo"]) / s["Z"] < tol or abs(s["tau"] - s["C_hi"]) / s["Z"] < tol, \

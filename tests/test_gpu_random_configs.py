@@ -4,15 +4,15 @@ dtype, sequence strides, partial windows, sequence ids and base positions,
 each through sv_verify_window, sv_verify_window_early_exit (which must equal
 the full window bit for bit) and sv_verify_greedy (bit-exact).  Then random
 token trees (random parent arrays up to 64 nodes) through sv_verify_tree in
-its three modes.  Margin cases are counted; the sweep allows at most one per
-configuration."""
+its three modes.  Margin cases are counted; each must be one, and their number
+is bounded by max_margins (one plus one per 50 sequences)."""
 import numpy as np
 import pytest
 import torch
 
 import draft_token_verification_06_amd as sv
 from draft_token_verification_06_amd import synth
-from gpu_common import check_greedy, check_tree, check_tree_walk, check_window
+from gpu_common import check_greedy, check_tree, check_tree_walk, check_window, max_margins
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -46,10 +46,11 @@ def test_random_window_configuration(k):
     full = sv.verify_window(d["target"], d["draft"], d["tokens"], seed=seed, tag=tag, window_len=wl,
                             seq_ids=sid, base_pos=bp, return_probs=True)
     n, m = check_window(d, full, seed=seed, tag=tag, window_len=wl, seq_ids=sid, base_pos=bp)
-    assert m <= 1
+    assert m <= max_margins(B), m
     ee = sv.verify_window(d["target"], d["draft"], d["tokens"], seed=seed, tag=tag, window_len=wl,
                           seq_ids=sid, base_pos=bp, return_probs=True, early_exit=True)
-    assert torch.equal(ee.n_accepted, full.n_accepted) and torch.equal(ee.out_tokens, full.out_tokens)
+    assert torch.equal(ee.n_accepted, full.n_accepted) and torch.equal(ee.out_tokens, full.out_tokens), \
+        "early exit differs from the full window"
     g = sv.verify_greedy(d["target"], d["tokens"], window_len=wl)
     check_greedy(d, g, window_len=wl)
 
@@ -70,7 +71,7 @@ def test_random_tree_configuration(k):
     for mode in ("greedy", "stochastic"):
         res = sv.verify_tree(d["target"], d["draft"], d["tokens"], d["parent"], mode=mode, seed=seed)
         n, m = check_tree(d, res, mode, seed=seed)
-        assert m <= 1
+        assert m <= max_margins(B), m
     res = sv.verify_tree(d["target"], d["draft"], d["tokens"], d["parent"], mode="multi_candidate", seed=seed)
     n, m, rej = check_tree_walk(d, res, seed=seed)
-    assert m <= 1
+    assert m <= max_margins(B), m
