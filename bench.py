@@ -151,6 +151,27 @@ def main():
     rs_ms = event_time_ms(torch, lambda it=iter(range(10 ** 9)): step(next(it), sv.api.SV_PART_ROW_STATS), reps)
     ds_ms = event_time_ms(torch, lambda it=iter(range(10 ** 9)): step(next(it), sv.api.SV_PART_DECIDE_SAMPLE), reps)
     full_ms = event_time_ms(torch, lambda it=iter(range(10 ** 9)): step(next(it)), reps)
+    # per acceptance level: whole calls on each batch, HIP events, median
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for k, (e0, e1) in enumerate(ev):
+        e0.record(s)
+        step(k)
+        e1.record(s)
+    torch.cuda.synchronize()
+    call_us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+    window_alpha = {}
+    for a, alpha in enumerate(ALPHAS):
+        t_us = float(np.median(call_us[a::len(ALPHAS)]))
+        n = ref[a][0]
+        ok = n >= 0
+        window_alpha[str(alpha)] = {
+            "us": t_us,
+            "verified_drafts_per_s": B * GAMMA / (t_us * 1e-6),
+            "accepted_per_s": float(n[ok].sum()) / (t_us * 1e-6),
+            "emitted_per_s": float((n[ok] + 1).sum()) / (t_us * 1e-6),
+            "GBps": B * (2 * GAMMA + 1) * V * 2 / (t_us * 1e-6) / 1e9,
+        }
     alg_bytes = B * (2 * GAMMA + 1) * V * 2
     rs_gbps = alg_bytes / (rs_ms * 1e-3) / 1e9
     step_gbps = alg_bytes / (ms_per_step * 1e-3) / 1e9
@@ -212,6 +233,9 @@ def main():
             "B": B, "gamma": GAMMA, "V": V, "alphas": list(ALPHAS),
             "input_bytes_per_step": alg_bytes,
         },
+        "accepted_per_s": float(np.mean([r[0][r[0] >= 0].sum() for r in ref])) / (ms_per_step * 1e-3),
+        "emitted_per_s": float(np.mean([(r[0][r[0] >= 0] + 1).sum() for r in ref])) / (ms_per_step * 1e-3),
+        "per_alpha": window_alpha,
         "achieved_GBps_step": step_gbps,
         "frac_of_hbm_peak_step": step_gbps / HBM_PEAK_GBPS,
         "roofline": {
