@@ -63,8 +63,12 @@ def kernel_sha():
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # Warm-up reaches the GPU's steady state: after an idle period the first
+    # ~200 back-to-back calls run up to 25% slower while the device's power
+    # management settles, then the call time holds flat over thousands of
+    # calls.  300 warm-up steps take ~60 ms, 1000 timed steps ~190 ms.
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle timing on the host (baseline only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
