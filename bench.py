@@ -92,6 +92,22 @@ def event_time_ms(torch, fn, reps):
     return sum(a.elapsed_time(b) for a, b in ev) / reps
 
 
+def event_span_ms(torch, fn, reps):
+    """Average duration of fn() over reps back-to-back launches: one pair of
+    HIP events brackets the whole run, so per-launch event overhead is not
+    counted, while the gaps between the launches are."""
+    s = torch.cuda.current_stream()
+    for _ in range(2):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    for _ in range(reps):
+        fn()
+    b.record(s)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -152,9 +168,9 @@ def main():
 
     # dominant kernel alone: row statistics, HIP events on its stream
     reps = max(len(ALPHAS), args.steps)
-    rs_ms = event_time_ms(torch, lambda it=iter(range(10 ** 9)): step(next(it), sv.api.SV_PART_ROW_STATS), reps)
-    ds_ms = event_time_ms(torch, lambda it=iter(range(10 ** 9)): step(next(it), sv.api.SV_PART_DECIDE_SAMPLE), reps)
-    full_ms = event_time_ms(torch, lambda it=iter(range(10 ** 9)): step(next(it)), reps)
+    rs_ms = event_span_ms(torch, lambda it=iter(range(10 ** 9)): step(next(it), sv.api.SV_PART_ROW_STATS), reps)
+    ds_ms = event_span_ms(torch, lambda it=iter(range(10 ** 9)): step(next(it), sv.api.SV_PART_DECIDE_SAMPLE), reps)
+    full_ms = event_span_ms(torch, lambda it=iter(range(10 ** 9)): step(next(it)), reps)
     # per acceptance level: whole calls on each batch, HIP events, median
     s = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
@@ -208,7 +224,7 @@ def main():
     probe_buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
     probe_buf.fill_(1)
     sink = sv.probe_read(probe_buf)
-    probe_ms = event_time_ms(torch, lambda: sv.probe_read(probe_buf, sink), 20)
+    probe_ms = event_span_ms(torch, lambda: sv.probe_read(probe_buf, sink), 50)
     probe_gbps = probe_buf.numel() / (probe_ms * 1e-3) / 1e9
     del probe_buf
     # a plain copy of known size (1 GiB), for scaling hardware byte counters
