@@ -120,3 +120,27 @@ def test_bad_host_arguments_return_status_without_device_work():
     assert L.sv_rollback(fake, fake, 4, 3, 8, 0, fake, 8, fake, 0, None) == -1
     assert L.sv_rollback(None, fake, 4, 3, 8, 1, fake, 8, fake, 0, None) == -1
     assert L.sv_probe_read(fake, 17, fake, None) == -1
+
+
+def test_binding_rejects_host_tensors_before_any_call():
+    """The Python binding checks tensors on the host: logits, tokens and
+    outputs in host memory are refused with ValueError, before the library is
+    asked to do anything."""
+    import torch
+    import draft_token_verification_06_amd as sv
+
+    B, gamma, V = 2, 3, 16
+    t = torch.zeros(B, gamma + 1, V, dtype=torch.bfloat16)
+    d = torch.zeros(B, gamma, V, dtype=torch.bfloat16)
+    toks = torch.zeros(B, gamma, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        sv.verify_window(t, d, toks)
+    with pytest.raises(ValueError):
+        sv.verify_greedy(t, toks)
+    with pytest.raises(ValueError):
+        sv.verify_window(t.to(torch.float64), d, toks)
+    with pytest.raises(ValueError):
+        sv.verify_window(t[:, :gamma], d, toks)          # target needs gamma + 1 rows
+    with pytest.raises(ValueError):
+        sv.rollback(torch.zeros(2, 3, 4, dtype=torch.int32), torch.zeros(2, 3, dtype=torch.int32), 1,
+                    torch.zeros(2, 4, dtype=torch.int32), torch.zeros(2, dtype=torch.int32))
