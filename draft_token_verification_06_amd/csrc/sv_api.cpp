@@ -403,9 +403,10 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
     launch_tree_walk(dtype, A, B, stream);
     return launch_status();
   }
-  launch_tree_decide(dtype, A, B, stream);
   if (mode == SV_TREE_STOCHASTIC)
-    launch_tree_finish(dtype, jobs, B, V, reinterpret_cast<float *>(wsb + L.spart_off), L.cmax, stream);
+    launch_tree_decide_draw(dtype, A, B, reinterpret_cast<float *>(wsb + L.spart_off), L.cmax, stream);
+  else
+    launch_tree_decide(dtype, A, B, stream);
   return launch_status();
 }
 

@@ -318,11 +318,14 @@ __global__ void __launch_bounds__(kWave) k_greedy_decide(GreedyArgs A) {
 // ---------------------------------------------------------------------------
 // Decide: token tree (one thread per node, N <= 256)
 // ---------------------------------------------------------------------------
+// The tree decision of sequence b by the calling workgroup: thread v < N
+// examines node v; threads past kTreeMaxNodes only join the barriers.  When
+// `write` is set the outputs are written.  The sampling job (stochastic mode)
+// goes to *job, which may be null in greedy mode; an invalid token gives
+// job->mode = JOB_NONE.
 template <int DT>
-__global__ void __launch_bounds__(kTreeMaxNodes) k_tree_decide(TreeArgs A) {
+__device__ void tree_decide(const TreeArgs &A, int b, int v, bool write, SampleJob *job_out) {
   using E = Elt<DT>;
-  const int b = blockIdx.x;
-  const int v = threadIdx.x;
   const int N = A.meta.N;
   const int D = A.meta.max_depth;
   int32_t *out_t = A.out_tokens + static_cast<int64_t>(b) * (D + 1);
@@ -346,13 +349,15 @@ __global__ void __launch_bounds__(kTreeMaxNodes) k_tree_decide(TreeArgs A) {
   }
   const bool bad = v >= 1 && v < N && (tok < 0 || tok >= A.V);
   if (__syncthreads_or(bad)) {
-    for (int k = v; k <= D; k += kTreeMaxNodes) out_t[k] = -1;
-    for (int k = v; k < D; k += kTreeMaxNodes) out_n[k] = -1;
-    if (v == 0) {
-      A.n_accepted[b] = -1;
-      A.best_node[b] = -1;
-      if (A.jobs) A.jobs[b].mode = JOB_NONE;
+    if (write) {
+      for (int k = v; k <= D; k += kTreeMaxNodes) out_t[k] = -1;
+      for (int k = v; k < D; k += kTreeMaxNodes) out_n[k] = -1;
+      if (v == 0) {
+        A.n_accepted[b] = -1;
+        A.best_node[b] = -1;
+      }
     }
+    if (v == 0 && job_out) job_out->mode = JOB_NONE;
     return;
   }
   const int64_t row_bytes = static_cast<int64_t>(A.V) * E::kBytes;
@@ -409,14 +414,18 @@ __global__ void __launch_bounds__(kTreeMaxNodes) k_tree_decide(TreeArgs A) {
   __syncthreads();
   const int best = s_best;
   const int nd = A.meta.depth[best];
-  for (int k = v; k < D; k += kTreeMaxNodes) out_n[k] = k < nd ? s_path[k] : -1;
-  for (int k = v; k <= D; k += kTreeMaxNodes)
-    if (k != nd) out_t[k] = k < nd ? toks[s_path[k]] : -1;
+  if (write) {
+    for (int k = v; k < D; k += kTreeMaxNodes) out_n[k] = k < nd ? s_path[k] : -1;
+    for (int k = v; k <= D; k += kTreeMaxNodes)
+      if (k != nd) out_t[k] = k < nd ? toks[s_path[k]] : -1;
+  }
   if (v == 0) {
-    A.n_accepted[b] = nd;
-    A.best_node[b] = best;
+    if (write) {
+      A.n_accepted[b] = nd;
+      A.best_node[b] = best;
+    }
     if (A.mode == 0) {
-      out_t[nd] = row_argmax(prow + best * A.S, A.S).i;
+      if (write) out_t[nd] = row_argmax(prow + best * A.S, A.S).i;
     } else {
       SampleJob job{};
       job.t_row = t0 + best * row_bytes;
@@ -436,9 +445,16 @@ __global__ void __launch_bounds__(kTreeMaxNodes) k_tree_decide(TreeArgs A) {
           A.seed, A.tag);
       job.v = uniform24(r.c1);
       job.out_slot = out_t + nd;
-      A.jobs[b] = job;
+      *job_out = job;
     }
   }
+}
+
+// Standalone decision, one 256-thread workgroup per sequence (greedy trees).
+template <int DT>
+__global__ void __launch_bounds__(kTreeMaxNodes) k_tree_decide(TreeArgs A) {
+  const int b = blockIdx.x;
+  tree_decide<DT>(A, b, threadIdx.x, true, A.jobs ? A.jobs + b : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -745,23 +761,32 @@ __device__ __forceinline__ int sample_job(const SampleJob &job, int V, float *s_
   return draw_from_sums<DT, false>(job, V, C, 0, s_cs, tid);
 }
 
-// Where the draw's job comes from: the jobs array (tree, or an early-exit
-// sequence decided in an earlier block), the window decision (wave 0), or
-// the early-exit decision of the last position block [A.stage_lo, gamma]
-// (wave 0, for sequences still verifying).  `write` gates the outputs.
-enum : int { SRC_JOBS = 0, SRC_WINDOW = 1, SRC_STAGE = 2 };
+// Where the draw's job comes from: the jobs array (an early-exit sequence
+// decided in an earlier block, or the LM-head path), the window decision
+// (wave 0), the early-exit decision of the last position block
+// [A.stage_lo, gamma] (wave 0, for sequences still verifying), or the
+// stochastic tree decision (the first kTreeMaxNodes threads; A is then a
+// TreeArgs).  `write` gates the outputs.
+enum : int { SRC_JOBS = 0, SRC_WINDOW = 1, SRC_STAGE = 2, SRC_TREE = 3 };
 
 // Job of sequence b into s_job; returns whether it was decided here.
-template <int DT, int kSrc>
-__device__ __forceinline__ bool load_job(const WindowArgs &A, const SampleJob *jobs, int b, bool write,
+template <int DT, int kSrc, typename Args>
+__device__ __forceinline__ bool load_job(const Args &A, const SampleJob *jobs, int b, bool write,
                                          SampleJob *s_job, int tid) {
   bool decided = false;
-  if (kSrc == SRC_WINDOW) {
+  if constexpr (kSrc == SRC_TREE) {
+    tree_decide<DT>(A, b, tid, write, s_job);  // every thread joins its barriers
+    decided = true;
+  } else if constexpr (kSrc == SRC_WINDOW) {
     if (tid < kWave) window_decide<DT>(A, b, tid, write, s_job);
     decided = true;
-  } else if (kSrc == SRC_STAGE && A.status[b] == kSeqVerifying) {
-    if (tid < kWave) stage_decide<DT>(A, b, tid, A.stage_lo, A.gamma + 1, A.status, write, false, s_job);
-    decided = true;
+  } else if constexpr (kSrc == SRC_STAGE) {
+    if (A.status[b] == kSeqVerifying) {
+      if (tid < kWave) stage_decide<DT>(A, b, tid, A.stage_lo, A.gamma + 1, A.status, write, false, s_job);
+      decided = true;
+    } else if (tid == 0) {
+      *s_job = jobs[b];
+    }
   } else if (tid == 0) {
     *s_job = jobs[b];
   }
@@ -771,8 +796,8 @@ __device__ __forceinline__ bool load_job(const WindowArgs &A, const SampleJob *j
 
 // One workgroup per sequence (large batches): decide, one pass over the
 // row(s) with chunk sums in LDS, draw.
-template <int DT, int kSrc>
-__global__ void __launch_bounds__(kFinThreads) k_finish(WindowArgs A, const SampleJob *__restrict__ jobs, int V) {
+template <int DT, int kSrc, typename Args = WindowArgs>
+__global__ void __launch_bounds__(kFinThreads) k_finish(Args A, const SampleJob *__restrict__ jobs, int V) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   __shared__ SampleJob s_job;
@@ -788,8 +813,8 @@ __global__ void __launch_bounds__(kFinThreads) k_finish(WindowArgs A, const Samp
 // Small batches, part 1, grid (B, G): workgroup g decides (redundantly, it is
 // cheap) and sums its share of the chunks into spart[b][c]; the g = 0
 // workgroup writes the window outputs and the job.
-template <int DT, int kSrc>
-__global__ void __launch_bounds__(kFinThreads) k_finish_part(WindowArgs A, SampleJob *__restrict__ jobs, int V,
+template <int DT, int kSrc, typename Args = WindowArgs>
+__global__ void __launch_bounds__(kFinThreads) k_finish_part(Args A, SampleJob *__restrict__ jobs, int V,
                                                             float *__restrict__ spart, int cmax) {
   const int b = blockIdx.x;
   const int g = blockIdx.y;
@@ -1062,14 +1087,15 @@ static int finish_split(int B, int V, int dtype) {
   return G < 1 ? 1 : G;
 }
 
-template <int DT, int kSrc>
-static void launch_finish_t(const WindowArgs &A, SampleJob *jobs, int B, int V, float *spart, int cmax,
+template <int DT, int kSrc, typename Args = WindowArgs>
+static void launch_finish_t(const Args &A, SampleJob *jobs, int B, int V, float *spart, int cmax,
                             hipStream_t st) {
   const int G = finish_split(B, V, DT);
   if (G == 1) {
-    hipLaunchKernelGGL((k_finish<DT, kSrc>), dim3(B), dim3(kFinThreads), 0, st, A, jobs, V);
+    hipLaunchKernelGGL((k_finish<DT, kSrc, Args>), dim3(B), dim3(kFinThreads), 0, st, A, jobs, V);
   } else {
-    hipLaunchKernelGGL((k_finish_part<DT, kSrc>), dim3(B, G), dim3(kFinThreads), 0, st, A, jobs, V, spart, cmax);
+    hipLaunchKernelGGL((k_finish_part<DT, kSrc, Args>), dim3(B, G), dim3(kFinThreads), 0, st, A, jobs, V, spart,
+                       cmax);
     hipLaunchKernelGGL(k_finish_select<DT>, dim3(B), dim3(kFinThreads), 0, st, jobs, V, spart, cmax);
   }
 }
@@ -1115,6 +1141,14 @@ void launch_tree_decide(int dtype, const TreeArgs &A, int B, hipStream_t st) {
 void launch_tree_finish(int dtype, SampleJob *jobs, int B, int V, float *spart, int cmax, hipStream_t st) {
   const WindowArgs none{};
   launch_finish<SRC_JOBS>(dtype, none, jobs, B, V, spart, cmax, st);
+}
+
+void launch_tree_decide_draw(int dtype, const TreeArgs &A, int B, float *spart, int cmax, hipStream_t st) {
+  switch (dtype) {
+    case DT_BF16: launch_finish_t<DT_BF16, SRC_TREE, TreeArgs>(A, A.jobs, B, A.V, spart, cmax, st); break;
+    case DT_F16: launch_finish_t<DT_F16, SRC_TREE, TreeArgs>(A, A.jobs, B, A.V, spart, cmax, st); break;
+    default: launch_finish_t<DT_F32, SRC_TREE, TreeArgs>(A, A.jobs, B, A.V, spart, cmax, st); break;
+  }
 }
 
 void launch_tree_walk(int dtype, const TreeArgs &A, int B, hipStream_t st) {

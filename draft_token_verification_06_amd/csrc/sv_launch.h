@@ -108,6 +108,8 @@ void launch_stage_finish(int dtype, const WindowArgs &A, int B, float *spart, in
 void launch_greedy_decide(const GreedyArgs &A, int B, hipStream_t st);
 void launch_tree_decide(int dtype, const TreeArgs &A, int B, hipStream_t st);
 void launch_tree_finish(int dtype, SampleJob *jobs, int B, int V, float *spart, int cmax, hipStream_t st);
+// Stochastic tree: the draw kernels decide each sequence themselves (no separate decision launch).
+void launch_tree_decide_draw(int dtype, const TreeArgs &A, int B, float *spart, int cmax, hipStream_t st);
 void launch_tree_walk(int dtype, const TreeArgs &A, int B, hipStream_t st);
 void launch_rollback(const RollbackArgs &A, int S, int stage, hipStream_t st);
 

@@ -23,6 +23,19 @@ def test_tree_branching_4_3_2_v50257_f16(mode):
 
 
 @pytest.mark.parametrize("mode", ["greedy", "stochastic"])
+def test_tree_branching_4_3_2_at_b256_sampled_sequences(mode):
+    # 256 sequences: the stochastic draw runs one workgroup per sequence, each
+    # deciding its own tree; the greedy tree runs the standalone decision
+    print("tree B=256", mode, flush=True)
+    d = synth.tree_batch(256, synth.bfs_tree((4, 3, 2)), 50257, dtype="f16", sigma=0.5, seed=4256,
+                         device=DEV)
+    res = sv.verify_tree(d["target"], d["draft"], d["tokens"], d["parent"], mode=mode, seed=11)
+    rows = list(range(0, 256, 11)) + [255]
+    n, m = check_tree(d, res, mode, seed=11, rows=rows)
+    assert m == 0 or (mode == "stochastic" and m <= 1)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "stochastic"])
 def test_tree_greedy_friendly_tokens_reach_deep_nodes(mode):
     # half of the node tokens equal the parent's argmax, so long paths occur
     d = synth.tree_batch(16, synth.bfs_tree((3, 2, 2, 1)), 3001, dtype="bf16", sigma=0.3,
