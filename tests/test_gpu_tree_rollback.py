@@ -78,6 +78,16 @@ def test_tree_invalid_node_token_and_bad_parent():
     with pytest.raises(sv.SvError) as e:
         sv.verify_tree(d["target"], d["draft"], toks, [-1, 0, 2, 1, 1, 2, 2], mode="greedy")
     assert e.value.status == -4
+    # the same with a vocabulary that splits the draw over several workgroups
+    # per sequence (every one of them decides; the first writes the outputs)
+    d = synth.tree_batch(3, synth.bfs_tree((2, 2)), 20000, dtype="f16", seed=5, device=DEV)
+    toks = d["tokens"].clone()
+    toks[2, 3] = -7
+    res = sv.verify_tree(d["target"], d["draft"], toks, d["parent"], mode="stochastic", seed=4)
+    assert res.n_accepted[2].item() == -1 and torch.all(res.out_tokens[2] == -1)
+    assert res.best_node[2].item() == -1
+    dd = dict(d, tokens=toks)
+    check_tree(dd, res, "stochastic", seed=4, rows=[0, 1])
 
 
 def _rollback_case(rng, S, K, cap):
