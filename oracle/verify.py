@@ -240,11 +240,15 @@ def verify_tree(target, draft, node_tokens, parent, mode, u_node, v_node):
     accepted node d (smallest index among equals) ends the path; the emitted
     token after d is argmax(target[d]) (greedy), a bonus draw from p_d when d
     has no children, or a draw from the renormalised max(0, p_d - q_d).
+    Also returned: ok[v] (v and its ancestors accepted), own[v] (v's own
+    test) and ratio[v] = P/Q of that test (stochastic mode), for reporting.
     """
     N = len(parent)
     depth, rank, has_child = tree_meta(parent)
     ok = [False] * N
     ok[0] = True
+    own = [True] * N           # node v's own test against its parent's row
+    ratio = [np.nan] * N       # P/Q of that test (stochastic mode)
     for v in range(1, N):
         w = parent[v]
         x = int(node_tokens[v])
@@ -255,7 +259,9 @@ def verify_tree(target, draft, node_tokens, parent, mode, u_node, v_node):
         else:
             P = float(softmax(target[w])[x])
             Q = float(softmax(draft[w])[x])
+            ratio[v] = P / Q if Q > 0 else np.inf
             acc = u_node[v] * Q < P
+        own[v] = bool(acc)
         ok[v] = ok[w] and acc
     d = 0
     for v in range(N):
@@ -291,6 +297,8 @@ def verify_tree(target, draft, node_tokens, parent, mode, u_node, v_node):
         "path": path,
         "out": [int(node_tokens[v]) for v in path] + [int(y)],
         "ok": ok,
+        "own": own,
+        "ratio": ratio,
         "sample": sample,
     }
 
