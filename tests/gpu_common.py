@@ -2,9 +2,12 @@
 
 Tolerances (speculative-sampling window, tree):
 * p(x), q(x) at examined drafts: within 1e-5 relative of the oracle;
-* accept decisions and drawn tokens identical, except cases whose margin is
-  under 1e-5: |u - P/Q| at an examined draft, or |tau - C| / Z at either end
-  of the drawn token's CDF interval.  Such cases are counted and returned.
+* accept decisions and drawn tokens identical, except margin cases, each tied
+  to the one place where GPU and oracle part ways: the first position (node,
+  sibling test) whose decision differs must have |u - P/Q| < 1e-5, and a
+  different token drawn from the same row must have |tau - C| / Z < 1e-5 at an
+  end of the oracle's CDF interval of its token.  Such cases are counted and
+  returned; nothing else is excused.
 Greedy verification, greedy trees and rollback are compared bit for bit.
 """
 import numpy as np
@@ -22,7 +25,8 @@ def max_margins(n_sequences):
     in float32, so a draw whose tau lies within about 1e-6 of a CDF boundary
     (relative to the total) can land on the other side; on flat rows of
     32000 tokens that is 1-2% of draws.  Every counted case is still checked
-    to be a margin case; this only bounds how many there may be."""
+    to be a margin case at the point of divergence; this only bounds how many
+    there may be."""
     return 1 + n_sequences // 50
 
 
@@ -30,18 +34,53 @@ def host_rows(t, dtype):
     return oracle.decode(to_host_bits(t), dtype)
 
 
-def _sample_margin(s):
+# Residual mass the library counts as none (it then draws from p): below
+# 2^-16, where float32 weights of two rows cannot be told from rounding.  A
+# draw from a residual whose exact mass is below twice that is a margin case.
+NO_RESIDUAL_MASS = 2.0 ** -16
+
+
+def _sample_margin(s, tol=MARGIN):
     if s is None:
         return False
+    if s.get("kind") == "residual" and s["Z"] < 2 * NO_RESIDUAL_MASS:
+        return True
     Z = s["Z"]
-    return abs(s["tau"] - s["C_lo"]) / Z < MARGIN or abs(s["tau"] - s["C_hi"]) / Z < MARGIN
+    return abs(s["tau"] - s["C_lo"]) / Z < tol or abs(s["tau"] - s["C_hi"]) / Z < tol
 
 
-def _decision_margin(o, upto):
-    for i, r in enumerate(o["ratio"][: upto + 1]):
-        if np.isfinite(r) and abs(o["u"][i] - r) < MARGIN:
-            return True
-    return False
+def _decision_margin(o, k, tol=MARGIN):
+    """The accept test at window position k (the first position where the
+    GPU's and the oracle's decisions differ) lies within the margin."""
+    if k >= len(o["ratio"]):
+        return False
+    r = o["ratio"][k]
+    return bool(np.isfinite(r) and abs(o["u"][k] - r) < tol)
+
+
+def window_divergence(o, n_gpu, out_gpu, gamma, tokens, V):
+    """None when the GPU's window outputs equal the oracle's; otherwise
+    ("decision", k) with k = min(n_gpu, n_oracle), the first position decided
+    differently, or ("draw", None) when n agrees and only the drawn token
+    differs.  Either way the GPU's row must be well formed for its own n
+    (drafts 0..n-1, a token in [0, V), then -1); raises otherwise."""
+    want = o["out"] + [-1] * (gamma + 1 - len(o["out"]))
+    if n_gpu == o["n"] and list(out_gpu) == want:
+        return None
+    assert 0 <= n_gpu <= gamma, n_gpu
+    assert list(out_gpu[:n_gpu]) == [int(x) for x in tokens[:n_gpu]], (list(out_gpu), o["out"])
+    assert 0 <= int(out_gpu[n_gpu]) < V, (list(out_gpu), o["out"])
+    assert all(int(x) == -1 for x in out_gpu[n_gpu + 1:]), (list(out_gpu), o["out"])
+    if n_gpu != o["n"]:
+        return ("decision", min(n_gpu, o["n"]))
+    return ("draw", None)
+
+
+def window_case_in_margin(o, div, tol_decision=MARGIN, tol_draw=MARGIN):
+    kind, k = div
+    if kind == "decision":
+        return _decision_margin(o, k, tol_decision)
+    return _sample_margin(o["sample"], tol_draw)
 
 
 def check_window(data, res, *, seed, tag=0, window_len=None, seq_ids=None, base_pos=None,
@@ -73,15 +112,10 @@ def check_window(data, res, *, seed, tag=0, window_len=None, seq_ids=None, base_
             for i in range(min(o["n"] + 1, length)):
                 assert abs(P_gpu[b, i] - o["P"][i]) <= PROB_RTOL * o["P"][i], (b, i, P_gpu[b, i], o["P"][i])
                 assert abs(Q_gpu[b, i] - o["Q"][i]) <= PROB_RTOL * o["Q"][i], (b, i, Q_gpu[b, i], o["Q"][i])
-        ng = int(n_gpu[b])
-        want = o["out"] + [-1] * (gamma + 1 - len(o["out"]))
-        if ng == o["n"] and list(out_gpu[b]) == want:
+        div = window_divergence(o, int(n_gpu[b]), out_gpu[b], gamma, toks[b], T.shape[1])
+        if div is None:
             continue
-        if ng != o["n"]:
-            assert _decision_margin(o, min(ng, o["n"])), (b, ng, o["n"], list(out_gpu[b]), o["out"])
-        else:
-            assert list(out_gpu[b][:ng]) == o["out"][:ng], (b, list(out_gpu[b]), o["out"])
-            assert _sample_margin(o["sample"]), (b, list(out_gpu[b]), o["out"], o["sample"])
+        assert window_case_in_margin(o, div), (b, div, int(n_gpu[b]), o["n"], list(out_gpu[b]), o["out"])
         margins += 1
     return len(rows), margins
 
@@ -103,7 +137,28 @@ def check_greedy(data, res, window_len=None, rows=None):
         assert list(out_gpu[b]) == o["out"] + [-1] * (gamma + 1 - len(o["out"])), b
 
 
-def check_tree(data, res, mode, *, seed=0, tag=0, rows=None):
+def _tree_key(depth, v):
+    """Order of the deepest-node choice: deeper first, then smaller index."""
+    return (depth[v], -v)
+
+
+def _tree_path(parent, v):
+    path = []
+    while v > 0:
+        path.append(v)
+        v = parent[v]
+    return path[::-1]
+
+
+def check_tree(data, res, mode, *, seed=0, tag=0, seq_ids=None, base_pos=None, rows=None):
+    """Compares sv_verify_tree (GREEDY or STOCHASTIC) with oracle.verify_tree.
+    Greedy is bit-exact.  In stochastic mode an end node d_g that differs from
+    the oracle's d_o is excused only by the node whose test the two sides must
+    have decided differently: if d_g ranks above d_o (deeper, or as deep with a
+    smaller index), every node on d_g's path that the oracle rejected; if it
+    ranks below, some node on d_o's path (the GPU rejected at least one of
+    them).  With the same end node, a different drawn token must be a draw
+    margin.  Returns (n_checked, n_margin_cases)."""
     dtype = data["dtype"]
     parent = data["parent"]
     B, N = data["tokens"].shape
@@ -115,11 +170,15 @@ def check_tree(data, res, mode, *, seed=0, tag=0, rows=None):
     best_gpu = res.best_node.cpu().numpy()
     out_gpu = res.out_tokens.cpu().numpy()
     nodes_gpu = res.out_nodes.cpu().numpy()
+    sid = seq_ids.cpu().numpy() if seq_ids is not None else None
+    bp = base_pos.cpu().numpy() if base_pos is not None else None
     margins = 0
     for b in rows:
         T = host_rows(data["target"][b], dtype)
         Dl = host_rows(data["draft"][b], dtype) if mode == "stochastic" else None
-        un, vn = oracle.tree_uniforms(seed, tag, b, 0, depth, rank)
+        s = int(sid[b]) if sid is not None else b
+        base = int(bp[b]) if bp is not None else 0
+        un, vn = oracle.tree_uniforms(seed, tag, s, base, depth, rank)
         o = oracle.verify_tree(T, Dl, toks[b], parent, mode, un, vn)
         want_t = o["out"] + [-1] * (D + 1 - len(o["out"]))
         want_n = o["path"] + [-1] * (D - len(o["path"]))
@@ -128,33 +187,36 @@ def check_tree(data, res, mode, *, seed=0, tag=0, rows=None):
         if same:
             continue
         assert mode == "stochastic", (b, list(out_gpu[b]), want_t)
-        # a different path needs a node decided within the margin
-        depth_margin = False
-        for v in range(1, N):
-            wpar = parent[v]
-            P = oracle.softmax(T[wpar])[toks[b][v]]
-            Q = oracle.softmax(Dl[wpar])[toks[b][v]]
-            if Q > 0 and abs(un[v] - P / Q) < MARGIN:
-                depth_margin = True
-        if int(best_gpu[b]) == o["best"]:
-            assert list(out_gpu[b][:o["n"]]) == o["out"][:o["n"]]
-            assert depth_margin or _sample_margin(o["sample"]), (b, list(out_gpu[b]), want_t)
+        dg, do = int(best_gpu[b]), o["best"]
+        assert 0 <= dg < N, (b, dg)
+        # the GPU's outputs must describe its own end node consistently
+        gpath = _tree_path(parent, dg)
+        assert int(n_gpu[b]) == depth[dg], (b, int(n_gpu[b]), dg)
+        assert list(nodes_gpu[b]) == gpath + [-1] * (D - len(gpath)), (b, list(nodes_gpu[b]), gpath)
+        assert list(out_gpu[b][:depth[dg]]) == [int(toks[b][v]) for v in gpath], b
+        assert list(out_gpu[b][depth[dg] + 1:]) == [-1] * (D - depth[dg]), b
+
+        def near(v):
+            return bool(np.isfinite(o["ratio"][v]) and abs(un[v] - o["ratio"][v]) < MARGIN)
+
+        if dg == do:
+            assert _sample_margin(o["sample"]), (b, list(out_gpu[b]), want_t, o["sample"])
+        elif _tree_key(depth, dg) > _tree_key(depth, do):
+            rejected = [v for v in gpath if not o["own"][v]]
+            assert rejected and all(near(v) for v in rejected), (b, dg, do, rejected)
         else:
-            assert depth_margin, (b, int(best_gpu[b]), o["best"])
+            assert any(near(v) for v in o["path"]), (b, dg, do, o["path"])
         margins += 1
     return len(rows), margins
 
 
-def _walk_decision_margin(tests):
+def _walk_test_in_margin(t):
     """A sibling test decided within the margin: |u - r(x)/q(x)| scaled by the
     condition of the float32 closed form (p(x) + shift q(x)) / (q(x) mass)."""
-    for t in tests:
-        if t["q"] <= 0.0 or not np.isfinite(t["ratio"]):
-            continue
-        cond = (t["p"] + t["shift"] * t["q"]) / (t["q"] * t["mass"])
-        if abs(t["u"] - t["ratio"]) < MARGIN * max(1.0, cond):
-            return True
-    return False
+    if t["q"] <= 0.0 or not np.isfinite(t["ratio"]):
+        return False
+    cond = (t["p"] + t["shift"] * t["q"]) / (t["q"] * t["mass"])
+    return bool(abs(t["u"] - t["ratio"]) < MARGIN * max(1.0, cond))
 
 
 def _walk_sample_margin(s):
@@ -165,6 +227,23 @@ def _walk_sample_margin(s):
     Z = s["Z"]
     tol = MARGIN * (1.0 + s["shift"]) / s["mass"]
     return abs(s["tau"] - s["C_lo"]) / Z < tol or abs(s["tau"] - s["C_hi"]) / Z < tol
+
+
+def _walk_divergent_test(o, gpath):
+    """The sibling test the GPU and the oracle must have decided differently:
+    at the first depth where the two paths part, the earlier (in sibling order,
+    which is index order) of the two accepted children, a missing child coming
+    last.  The oracle tested that child; returns its test record."""
+    opath = o["path"]
+    k = 0
+    while k < len(opath) and k < len(gpath) and opath[k] == gpath[k]:
+        k += 1
+    w = opath[k - 1] if k > 0 else 0
+    v = min(p[k] for p in (opath, gpath) if k < len(p))
+    for t in o["tests"]:
+        if t["node"] == v and t["parent"] == w:
+            return t
+    raise AssertionError(f"node {v} was never tested under {w}: paths {opath} / {gpath}")
 
 
 def check_tree_walk(data, res, *, seed=0, tag=0, seq_ids=None, base_pos=None, rows=None):
@@ -201,10 +280,14 @@ def check_tree_walk(data, res, *, seed=0, tag=0, seq_ids=None, base_pos=None, ro
             continue
         if int(best_gpu[b]) == o["best"] and list(nodes_gpu[b]) == want_n:
             assert list(out_gpu[b][:o["n"]]) == o["out"][:o["n"]]
-            assert _walk_sample_margin(o["sample"]) or _walk_decision_margin(o["tests"]), \
-                (b, list(out_gpu[b]), want_t, o["sample"])
+            assert _walk_sample_margin(o["sample"]), (b, list(out_gpu[b]), want_t, o["sample"])
         else:
-            assert _walk_decision_margin(o["tests"]), (b, list(nodes_gpu[b]), want_n)
+            dg = int(best_gpu[b])
+            assert 0 <= dg < N, (b, dg)
+            gpath = _tree_path(parent, dg)
+            assert list(nodes_gpu[b]) == gpath + [-1] * (D - len(gpath)), (b, list(nodes_gpu[b]), gpath)
+            t = _walk_divergent_test(o, gpath)
+            assert _walk_test_in_margin(t), (b, gpath, o["path"], t)
         margins += 1
     return len(rows), margins, rejected
 
@@ -245,19 +328,15 @@ def check_lmhead(data, res, *, seed, tag=0, window_len=None, rows=None):
             for i in range(min(o["n"] + 1, length)):
                 assert abs(P_gpu[b, i] - o["P"][i]) <= tp * o["P"][i], (b, i, P_gpu[b, i], o["P"][i], tp)
                 assert abs(Q_gpu[b, i] - o["Q"][i]) <= tq * o["Q"][i], (b, i, Q_gpu[b, i], o["Q"][i], tq)
-        ng = int(n_gpu[b])
-        want = o["out"] + [-1] * (gamma + 1 - len(o["out"]))
-        if ng == o["n"] and list(out_gpu[b]) == want:
+        div = window_divergence(o, int(n_gpu[b]), out_gpu[b], gamma, toks[b], Wt.shape[0])
+        if div is None:
             continue
-        if ng != o["n"]:
-            near = any(np.isfinite(r) and abs(o["u"][i] - r) < MARGIN + (tp + tq) * r
-                       for i, r in enumerate(o["ratio"][: min(ng, o["n"]) + 1]))
-            assert near, (b, ng, o["n"], list(out_gpu[b]), o["out"])
+        if div[0] == "decision":
+            k = div[1]
+            r = o["ratio"][k] if k < len(o["ratio"]) else np.inf
+            ok = bool(np.isfinite(r) and abs(o["u"][k] - r) < MARGIN + (tp + tq) * r)
         else:
-            assert list(out_gpu[b][:ng]) == o["out"][:ng], (b, list(out_gpu[b]), o["out"])
-            s = o["sample"]
-            tol = MARGIN + 2 * (tp + tq)
-            assert abs(s["tau"] - s["C_lo"]) / s["Z"] < tol or abs(s["tau"] - s["C_hi"]) / s["Z"] < tol, \
-                (b, list(out_gpu[b]), o["out"], s)
+            ok = _sample_margin(o["sample"], MARGIN + 2 * (tp + tq))
+        assert ok, (b, div, int(n_gpu[b]), o["n"], list(out_gpu[b]), o["out"], o["sample"])
         margins += 1
     return len(rows), margins

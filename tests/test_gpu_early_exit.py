@@ -6,7 +6,7 @@ import torch
 
 import draft_token_verification_06_amd as sv
 from draft_token_verification_06_amd import synth
-from gpu_common import check_window
+from gpu_common import check_window, max_margins
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -34,8 +34,9 @@ def test_early_exit_b256_gamma8_v128256_bf16(alpha):
     print("early exit alpha", alpha, flush=True)
     d = synth.window_config5(alpha, device=DEV)
     res = _same_as_full_window(d, seed=0)
-    n, m = check_window(d, res, seed=0, rows=[0, 17, 101, 255])
-    assert m <= 1
+    n, m = check_window(d, res, seed=0)
+    print("early exit alpha", alpha, "margin cases", m, "of", n, flush=True)
+    assert n == 256 and m <= max_margins(256)
 
 
 def test_early_exit_small_configs():
@@ -95,9 +96,9 @@ def test_large_batch_ragged_rows_and_partial_windows(dtype, V):
     wl = torch.tensor([b % (gamma + 1) for b in range(B)], dtype=torch.int32, device=DEV)
     wl[9] = -1
     res = _same_as_full_window(d, seed=8, window_len=wl)
-    rows = [b for b in range(0, B, 9) if b != 9]
+    rows = [b for b in range(B) if b != 9]
     n, m = check_window(d, res, seed=8, window_len=wl, rows=rows)
-    assert m <= 1 and res.n_accepted[9].item() == -1
+    assert m <= max_margins(B) and res.n_accepted[9].item() == -1
     # the two-kernel form of the same call, through the split entry point
     ws = sv.workspace(sv.SV_OP_WINDOW, B, gamma, V, d["target"].dtype, DEV)
     two = sv.WindowResult(torch.empty(B, dtype=torch.int32, device=DEV),
@@ -107,4 +108,4 @@ def test_large_batch_ragged_rows_and_partial_windows(dtype, V):
         sv.verify_window(d["target"], d["draft"], d["tokens"], seed=8, window_len=wl, ws=ws,
                          out=two, part=part)
     n, m = check_window(d, two, seed=8, window_len=wl, rows=rows)
-    assert m <= 1
+    assert m <= max_margins(B)

@@ -68,10 +68,17 @@ def test_random_tree_configuration(k):
     print("random tree", k, N, B, V, dtype, sigma, flush=True)
     d = synth.tree_batch(B, parent, V, dtype=dtype, sigma=sigma, seed=3100 + k, device=DEV)
     seed = int(rng.integers(0, 2 ** 40))
+    # odd configurations key their uniforms by caller ids, positions and a tag
+    keys = {}
+    if k % 2:
+        keys = dict(tag=int(rng.integers(1, 2 ** 32)),
+                    seq_ids=torch.from_numpy(rng.integers(0, 2 ** 40, B).astype(np.int64)).to(DEV),
+                    base_pos=torch.from_numpy(rng.integers(0, 10 ** 6, B).astype(np.int64)).to(DEV))
     for mode in ("greedy", "stochastic"):
-        res = sv.verify_tree(d["target"], d["draft"], d["tokens"], d["parent"], mode=mode, seed=seed)
-        n, m = check_tree(d, res, mode, seed=seed)
+        res = sv.verify_tree(d["target"], d["draft"], d["tokens"], d["parent"], mode=mode, seed=seed, **keys)
+        n, m = check_tree(d, res, mode, seed=seed, **keys)
         assert m <= max_margins(B), m
-    res = sv.verify_tree(d["target"], d["draft"], d["tokens"], d["parent"], mode="multi_candidate", seed=seed)
-    n, m, rej = check_tree_walk(d, res, seed=seed)
+    res = sv.verify_tree(d["target"], d["draft"], d["tokens"], d["parent"], mode="multi_candidate", seed=seed,
+                         **keys)
+    n, m, rej = check_tree_walk(d, res, seed=seed, **keys)
     assert m <= max_margins(B), m
