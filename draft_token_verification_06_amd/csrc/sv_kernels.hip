@@ -23,6 +23,14 @@
 
 namespace sv {
 
+// Residual mass max(0, p - cq q) below which a draw counts it as none and
+// draws from p.  Weights are formed as 2^(x log2e - c) with offsets c of
+// magnitude ~10-60 rounded to float32, so two rows holding the same logits
+// can differ by ~1e-6 in every weight when their offsets round differently
+// (the row pass reduces rows at different 16-byte alignments in different
+// orders); mass below 2^-16 cannot be told apart from that rounding.
+constexpr float kNoResidualMass = 0x1p-16f;
+
 // Combine the S segment results of one row, in segment order.  The loads go
 // out kSegBatch at a time ahead of their combines, so a row costs
 // ceil(S / kSegBatch) round trips, not S.
@@ -652,8 +660,9 @@ __device__ __forceinline__ void chunk_totals(const float *wp, int c_begin, int c
 // Z = the last one, tau = v * Z, and the chunk holding tau is the first whose
 // prefix exceeds it; then the first k of that chunk whose running sum exceeds
 // tau (w_k > 0).  If rounding leaves no such chunk, the last chunk with mass;
-// if it leaves no such k, the chunk's last k with w_k > 0.  cs must be visible
-// to the whole workgroup.
+// if it leaves no such k, the chunk's last k with w_k > 0.  Returns -1 (every
+// thread) when the weights have no mass: none at all, or a residual whose
+// mass is below kNoResidualMass.  cs must be visible to the whole workgroup.
 template <int DT, bool kVec>
 __device__ int draw_from_sums(const SampleJob &job, int V, int C, int h, const float *cs, int tid) {
   using G = FinGeom<DT, kVec>;
@@ -688,7 +697,8 @@ __device__ int draw_from_sums(const SampleJob &job, int V, int C, int h, const f
       const uint64_t hit = __ballot(c < C && s_pref[c] > tau);
       if (hit) chunk = c0 + __builtin_ctzll(hit);
     }
-    if (chunk < 0) chunk = last_mass >= 0 ? last_mass : 0;  // rounding left tau at or past the total
+    if (chunk < 0) chunk = last_mass;  // rounding left tau at or past the total (-1: no mass)
+    if (!(Z > 0.0f) || (job.mode == JOB_RESIDUAL && Z < kNoResidualMass)) chunk = -1;
     if (lane == 0) {
       s_chunk = chunk;
       s_base = chunk > 0 ? s_pref[chunk - 1] : 0.0f;
@@ -699,6 +709,7 @@ __device__ int draw_from_sums(const SampleJob &job, int V, int C, int h, const f
   }
   __syncthreads();
   const int chunk = s_chunk;
+  if (chunk < 0) return -1;
   float w[G::E];
   thread_weights<DT, kVec>(job, V, chunk, tid, h, w);
   float ts = 0.0f;
@@ -736,14 +747,26 @@ __device__ int draw_from_sums(const SampleJob &job, int V, int C, int h, const f
   if (has_last && lane == 63 - __builtin_clzll(has_last)) atomicMax(&s_last, last);
   __syncthreads();
   int y = s_cand != INT_MAX ? s_cand : s_last;
-  if (y < 0) y = max(0, chunk * G::CH - h);  // no mass anywhere: only reachable with invalid logits
+  if (y < 0) y = max(0, chunk * G::CH - h);  // the chunk had mass but rounding hid it from every slot
   return y;
 }
 
+// A residual job drawn as a bonus from the target row: what a draw with no
+// residual mass falls back to (the rejected draft had p = q = 0 and the two
+// rows are identical, or identical to within the rounding of their
+// normalisers).
+__device__ __forceinline__ SampleJob as_bonus(SampleJob job) {
+  job.mode = JOB_BONUS;
+  job.d_row = nullptr;
+  job.cd = 0.0f;
+  job.cq = 0.0f;
+  return job;
+}
+
 // Sampling pass of one job over chunks [0, C) and the draw, by the whole
-// workgroup; chunk sums in s_cs.
+// workgroup; chunk sums in s_cs.  Returns -1 when the weights have no mass.
 template <int DT>
-__device__ __forceinline__ int sample_job(const SampleJob &job, int V, float *s_wp, float *s_cs, int tid) {
+__device__ __forceinline__ int sample_pass(const SampleJob &job, int V, float *s_wp, float *s_cs, int tid) {
   const int h = job_shift(job, Elt<DT>::kBytes);
   if (h >= 0) {
     const int C = finish_chunks<DT, true>(V, h);
@@ -759,6 +782,15 @@ __device__ __forceinline__ int sample_job(const SampleJob &job, int V, float *s_
   chunk_totals(s_wp, 0, C, s_cs, tid);
   __syncthreads();
   return draw_from_sums<DT, false>(job, V, C, 0, s_cs, tid);
+}
+
+// The draw of one job; a residual without mass is drawn from p instead.
+template <int DT>
+__device__ __forceinline__ int sample_job(const SampleJob &job, int V, float *s_wp, float *s_cs, int tid) {
+  const int y = sample_pass<DT>(job, V, s_wp, s_cs, tid);
+  if (y >= 0) return y;
+  __syncthreads();  // s_cs and the draw's LDS are reused
+  return sample_pass<DT>(as_bonus(job), V, s_wp, s_cs, tid);
 }
 
 // Where the draw's job comes from: the jobs array (an early-exit sequence
@@ -847,6 +879,7 @@ __global__ void __launch_bounds__(kFinThreads) k_finish_select(const SampleJob *
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   __shared__ float s_cs[kFinMaxChunks];
+  __shared__ float s_wp[kFinMaxChunks * kFinWaves];  // only for a draw without residual mass
   static_assert(kFinMaxChunks <= kFinThreads, "one chunk sum per thread");
   // the chunk sums travel with the job load (cmax >= C whatever the shift)
   const float x = tid < cmax ? spart[static_cast<int64_t>(b) * cmax + tid] : 0.0f;
@@ -857,8 +890,12 @@ __global__ void __launch_bounds__(kFinThreads) k_finish_select(const SampleJob *
   const int C = vec ? finish_chunks<DT, true>(V, h) : finish_chunks<DT, false>(V, 0);
   if (tid < C) s_cs[tid] = x;
   __syncthreads();
-  const int y = vec ? draw_from_sums<DT, true>(job, V, C, h, s_cs, tid)
-                    : draw_from_sums<DT, false>(job, V, C, 0, s_cs, tid);
+  int y = vec ? draw_from_sums<DT, true>(job, V, C, h, s_cs, tid)
+              : draw_from_sums<DT, false>(job, V, C, 0, s_cs, tid);
+  if (y < 0) {  // no residual mass: this workgroup draws from p alone
+    __syncthreads();
+    y = sample_pass<DT>(as_bonus(job), V, s_wp, s_cs, tid);
+  }
   if (tid == 0) *job.out_slot = y;
 }
 
@@ -960,7 +997,7 @@ __global__ void __launch_bounds__(kFinThreads) k_tree_walk(TreeArgs A) {
       if (pending) {  // s_cs holds the chunk sums of max(0, p - c_try q)
         float z = 0.0f;
         for (int k = 0; k < pend_chunks; ++k) z += s_cs[k];
-        sums_ok = z > 0.0f;
+        sums_ok = z >= kNoResidualMass;
         if (sums_ok) {
           c = c_try;
           Z = z;
@@ -1029,8 +1066,12 @@ __global__ void __launch_bounds__(kFinThreads) k_tree_walk(TreeArgs A) {
       __syncthreads();
     }
     if (cmd == WALK_PASS) continue;
-    const int y = vec ? draw_from_sums<DT, true>(job, V, C, h, s_cs, tid)
-                      : draw_from_sums<DT, false>(job, V, C, 0, s_cs, tid);
+    int y = vec ? draw_from_sums<DT, true>(job, V, C, h, s_cs, tid)
+                : draw_from_sums<DT, false>(job, V, C, 0, s_cs, tid);
+    if (y < 0) {  // rounding left the residual without mass: draw from p_w
+      __syncthreads();
+      y = sample_pass<DT>(as_bonus(job), V, s_wp, s_cs, tid);
+    }
     const int n = s_nd;
     for (int k = tid; k < D; k += kFinThreads) out_n[k] = k < n ? s_path[k] : -1;
     for (int k = tid; k <= D; k += kFinThreads) out_t[k] = k < n ? s_tok[s_path[k]] : (k == n ? y : -1);

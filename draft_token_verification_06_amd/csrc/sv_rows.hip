@@ -203,7 +203,11 @@ __global__ void __launch_bounds__(kRowThreads) k_row_stats(RowSet rs, float2 *__
   stream_segment<DT, kRowThreads, kUnroll>(row, lo, hi, tid, acc);
 
   __shared__ float lds_m[kRowThreads / kWave], lds_s[kRowThreads / kWave];
-  const float2 res = acc.result(lds_m, lds_s, tid);
+  float2 res = acc.result(lds_m, lds_s, tid);
+  // A segment with no value above -inf has its first index as the first
+  // maximum, so a row of -inf values has argmax 0.
+  if constexpr (kArgmax)
+    if (__float_as_int(res.y) == INT_MAX) res.y = __int_as_float(lo);
   if (tid == 0) part[(b * rs.R_out + slot) * rs.S + seg] = res;
 }
 

@@ -6,7 +6,7 @@ import torch
 
 import draft_token_verification_06_amd as sv
 from draft_token_verification_06_amd import synth
-from gpu_common import check_window, check_greedy
+from gpu_common import check_greedy, check_tree, check_tree_walk, check_window, max_margins
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -224,3 +224,71 @@ def test_binding_rejects_malformed_outputs_and_workspaces():
     ref = sv.verify_window(d["target"], d["draft"], d["tokens"])
     torch.cuda.synchronize()
     assert torch.equal(r.n_accepted, ref.n_accepted) and torch.equal(r.out_tokens, ref.out_tokens)
+
+
+@pytest.mark.parametrize("B", [3, 256])
+def test_fully_masked_row_has_argmax_zero(B):
+    """A target row with no value above -inf: its first maximum is index 0, as
+    numpy's argmax (the oracle's) gives it, also when the row is reduced in
+    several segments (V = 100000 at B = 3 takes 4 segments per row)."""
+    gamma, V = 4, 100000
+    _say("masked row greedy B", B)
+    d = synth.window_batch(B, gamma, V, "bf16", target_sd=2.0, boost=4.0, sigma=0.5, seed=33,
+                           device=DEV)
+    t = d["target"].clone()
+    am = t.float().argmax(-1).to(torch.int32)
+    toks = d["tokens"].clone()
+    toks[:, :2] = am[:, :2]          # drafts 0 and 1 match, so row 2 is examined
+    toks[1, 2] = 5                   # sequence 1: draft 2 differs from argmax 0 -> emits 0
+    toks[0, 2] = 0                   # sequence 0: draft 2 equals argmax 0 -> accepted
+    t[:2, 2, :] = float("-inf")
+    d = dict(d, target=t.contiguous(), tokens=toks.contiguous())
+    g = sv.verify_greedy(d["target"], d["tokens"])
+    check_greedy(d, g)
+    assert g.out_tokens[1, 2].item() == 0 and g.n_accepted[1].item() == 2
+    assert g.n_accepted[0].item() >= 3
+
+
+@pytest.mark.parametrize("B", [3, 256])
+@pytest.mark.parametrize("dtype,V", [("bf16", 128256), ("f16", 50257), ("f32", 4099)])
+def test_rejected_draft_without_residual_mass_draws_from_p(B, dtype, V):
+    """A draft with p(x) = q(x) = 0 (masked in both rows) is rejected; when the
+    two rows are otherwise identical the residual max(0, p - q) has no mass
+    and the token is drawn from p, as in the oracle.  B = 3 takes the split
+    draw (the select kernel draws from p), B = 256 the one-workgroup draw."""
+    gamma = 3
+    _say("no residual mass", B, dtype, V)
+    d = synth.window_batch(B, gamma, V, dtype, target_sd=2.0, boost=3.0, sigma=0.5, seed=44,
+                           device=DEV)
+    t, dr, toks = d["target"].clone(), d["draft"].clone(), d["tokens"].clone()
+    sel = torch.arange(0, B, 2, device=DEV)           # every other sequence, at position 0
+    dr[sel, 0] = t[sel, 0]
+    x = toks[sel, 0].long()
+    t[sel, 0, x] = float("-inf")
+    dr[sel, 0, x] = float("-inf")
+    d = dict(d, target=t.contiguous(), draft=dr.contiguous(), tokens=toks.contiguous())
+    res = sv.verify_window(d["target"], d["draft"], d["tokens"], seed=6, return_probs=True)
+    n, m = check_window(d, res, seed=6)
+    assert m <= max_margins(B)
+    assert torch.all(res.n_accepted[sel] == 0)
+    ee = sv.verify_window(d["target"], d["draft"], d["tokens"], seed=6, early_exit=True)
+    assert torch.equal(ee.out_tokens, res.out_tokens)
+    # the same through a tree: root row identical in both logits, child 1 masked
+    parent = [-1, 0, 0, 1]
+    N = len(parent)
+    tt = synth.tree_batch(B, parent, V, dtype=dtype, sigma=0.5, seed=45, device=DEV)
+    T, Dt, nt = tt["target"].clone(), tt["draft"].clone(), tt["tokens"].clone()
+    Dt[:, 0] = T[:, 0]
+    for v in (1, 2):
+        xv = nt[:, v].long()
+        T[torch.arange(B, device=DEV), 0, xv] = float("-inf")
+        Dt[torch.arange(B, device=DEV), 0, xv] = float("-inf")
+    tt = dict(tt, target=T.contiguous(), draft=Dt.contiguous(), tokens=nt.contiguous())
+    for mode in ("stochastic", "multi_candidate"):
+        r = sv.verify_tree(tt["target"], tt["draft"], tt["tokens"], parent, mode=mode, seed=8)
+        assert torch.all(r.best_node == 0)
+        if mode == "stochastic":
+            n, m = check_tree(tt, r, mode, seed=8)
+        else:
+            n, m, _ = check_tree_walk(tt, r, seed=8)
+        assert m <= max_margins(B)

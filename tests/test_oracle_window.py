@@ -323,3 +323,21 @@ def test_greedy_longest_matching_prefix(np_rng):
         n_want = min(cut, length)
         assert r["n"] == n_want
         assert r["out"] == toks[:n_want] + [a[n_want]]
+
+
+def test_rejected_draft_without_residual_mass_draws_from_p():
+    """A draft with p(x) = q(x) = 0 is rejected (u * 0 < 0 fails); when the rows
+    are otherwise identical max(0, p - q) has no mass, and the replacement
+    follows p itself: its exact law over the uniform grid equals scipy's
+    softmax of the target row."""
+    from scipy.special import softmax as sp_softmax
+    rng = np.random.default_rng(19)
+    V, x = 8, 3
+    T = rng.normal(0, 1, (2, V))
+    D = T[:1].copy()
+    T[0, x] = D[0, x] = -np.inf
+    r = verify_window(T, D, [x], 1, [0.25], [0.5, 0.5])
+    assert r["n"] == 0 and r["sample"]["kind"] == "residual-empty"
+    law = _sample_law(lambda k: verify_window(T, D, [x], 1, [0.25], [k / GRID, 0.0])["out"][0], V)
+    assert np.allclose(law, sp_softmax(T[0]), atol=4 * V / GRID)
+    assert law[x] == 0.0
