@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     workspace_size,
     workspace,
     verify_window,
+    verify_window_noalloc,
     verify_window_lmhead,
     verify_greedy,
     verify_tree,
@@ -26,6 +27,6 @@ from .api import (  # noqa: F401
 
 __all__ = [
     "SvError", "WindowResult", "TreeResult", "workspace_size", "workspace",
-    "verify_window", "verify_window_lmhead", "verify_greedy", "verify_tree", "tree_max_depth", "rollback",
+    "verify_window", "verify_window_noalloc", "verify_window_lmhead", "verify_greedy", "verify_tree", "tree_max_depth", "rollback",
     "probe_read",
 ]

@@ -18,6 +18,8 @@ _SIGNATURES = {
     "sv_workspace_size": (_SZ, [_c.c_int, _I32, _I32, _I32, _c.c_int]),
     "sv_verify_window": (_c.c_int, [_P, _I64, _P, _I64, _c.c_int, _P, _P, _I32, _I32, _I32,
                                     _U64, _U64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "sv_verify_window_noalloc": (_c.c_int, [_P, _I64, _P, _I64, _c.c_int, _P, _P, _I32, _I32, _I32,
+                                            _U64, _U64, _P, _P, _P, _P, _P, _P, _P]),
     "sv_verify_window_early_exit": (_c.c_int, [_P, _I64, _P, _I64, _c.c_int, _P, _P, _I32, _I32, _I32,
                                                _U64, _U64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "sv_verify_window_part": (_c.c_int, [_c.c_int, _P, _I64, _P, _I64, _c.c_int, _P, _P, _I32, _I32,

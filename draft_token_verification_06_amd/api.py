@@ -170,6 +170,41 @@ def verify_window(target, draft, tokens, *, seed=0, tag=0, window_len=None, seq_
     return out
 
 
+def verify_window_noalloc(target, draft, tokens, *, seed=0, tag=0, window_len=None, seq_ids=None,
+                          base_pos=None, return_probs=False, out=None):
+    """sv_verify_window_noalloc: the stochastic window on the library's static
+    per-GPU scratch, with no workspace.  Calls on one GPU must not overlap."""
+    B, rows, V = target.shape
+    gamma = rows - 1
+    ts = _logits(target, gamma + 1, "target")
+    ds = _logits(draft, gamma, "draft")
+    if draft.dtype != target.dtype or draft.shape[0] != B or draft.shape[2] != V:
+        raise ValueError("draft must match target in dtype, batch and vocabulary")
+    _i32(tokens, (B, gamma), "tokens")
+    _optional(window_len, torch.int32, B, "window_len")
+    _optional(seq_ids, torch.int64, B, "seq_ids")
+    _optional(base_pos, torch.int64, B, "base_pos")
+    dev = target.device
+    _same_device(dev, draft=draft, tokens=tokens, window_len=window_len, seq_ids=seq_ids,
+                 base_pos=base_pos)
+    if out is None:
+        out = WindowResult(torch.empty(B, dtype=torch.int32, device=dev),
+                           torch.empty(B, gamma + 1, dtype=torch.int32, device=dev))
+        if return_probs:
+            out.p_draft = torch.empty(B, gamma, dtype=torch.float32, device=dev)
+            out.q_draft = torch.empty(B, gamma, dtype=torch.float32, device=dev)
+    else:
+        _check_window_out(out, B, gamma, dev)
+    with torch.cuda.device(dev):
+        _check(lib().sv_verify_window_noalloc(
+            _ptr(target), ts, _ptr(draft), ds, _DTYPE_CODE[target.dtype],
+            _ptr(tokens), _ptr(window_len), B, gamma, V,
+            ctypes.c_uint64(seed), ctypes.c_uint64(tag), _ptr(seq_ids), _ptr(base_pos),
+            _ptr(out.n_accepted), _ptr(out.out_tokens), _ptr(out.p_draft), _ptr(out.q_draft),
+            _stream(dev)))
+    return out
+
+
 def verify_window_lmhead(h_target, w_target, h_draft, w_draft, tokens, *, seed=0, tag=0,
                          window_len=None, seq_ids=None, base_pos=None, return_probs=False, ws=None):
     """Window verification on logits from hidden states, LM head fused:

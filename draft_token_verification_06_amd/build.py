@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspecverify.so")
 SOURCES = [os.path.join(CSRC, "sv_rows.hip"), os.path.join(CSRC, "sv_kernels.hip"),
-           os.path.join(CSRC, "sv_lmhead.hip"), os.path.join(CSRC, "sv_api.cpp")]
+           os.path.join(CSRC, "sv_lmhead.hip"), os.path.join(CSRC, "sv_noalloc.hip"),
+           os.path.join(CSRC, "sv_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

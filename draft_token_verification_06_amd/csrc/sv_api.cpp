@@ -95,6 +95,7 @@ const char *sv_strerror(int status) {
     case SV_EWORKSPACE: return "workspace missing, not 256-byte aligned, or too small";
     case SV_ETREE: return "malformed tree (parent[0] != -1, parent[v] not in [0, v), too many nodes or too deep)";
     case SV_ELAUNCH: return "kernel launch failed";
+    case SV_ESCRATCH: return "the call needs more workspace than the library's static scratch (SV_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

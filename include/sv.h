@@ -65,7 +65,8 @@ typedef enum {
   SV_EDTYPE = -2,     /* unknown dtype                                         */
   SV_EWORKSPACE = -3, /* workspace missing, misaligned (256 B) or too small    */
   SV_ETREE = -4,      /* malformed parent array, too many nodes or too deep    */
-  SV_ELAUNCH = -5     /* a kernel launch failed                                */
+  SV_ELAUNCH = -5,    /* a kernel launch failed                                */
+  SV_ESCRATCH = -6    /* the call needs more than SV_SCRATCH_BYTES of scratch  */
 } sv_status;
 
 typedef enum { SV_OP_WINDOW = 0, SV_OP_GREEDY = 1, SV_OP_TREE = 2, SV_OP_LMHEAD = 3 } sv_op;
@@ -77,6 +78,8 @@ typedef enum { SV_TREE_GREEDY = 0, SV_TREE_STOCHASTIC = 1, SV_TREE_MULTI_CANDIDA
 #define SV_LMHEAD_K_STEP 64
 #define SV_LMHEAD_MAX_HIDDEN 65536
 #define SV_TREE_MAX_DEPTH 64
+/* Device scratch of sv_verify_window_noalloc, per GPU (8 MiB). */
+#define SV_SCRATCH_BYTES (8u << 20)
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int sv_version(void);
@@ -113,6 +116,29 @@ int sv_verify_window(const void *target_logits, int64_t target_seq_stride,
                      int32_t *n_accepted, int32_t *out_tokens,
                      float *p_draft, float *q_draft,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* sv_verify_window for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, rule and outputs as sv_verify_window (bit-identical), minus
+ * the workspace: the library keeps one SV_SCRATCH_BYTES device array per GPU
+ * (a static device variable, held until the process ends) and uses it as the
+ * workspace.  Its address is looked up once per device, on the first call
+ * with that device current; the call allocates nothing.
+ *   Limit: sv_workspace_size(SV_OP_WINDOW, B, gamma, V, dtype) must not
+ *   exceed SV_SCRATCH_BYTES (B = 256, gamma = 8, V = 128256 needs 156 KiB);
+ *   larger calls return SV_ESCRATCH and enqueue nothing.
+ *   Every call on one GPU shares that array and no state survives between
+ *   calls, so calls that overlap on one GPU (different streams, or host
+ *   threads) race and must be serialised by the caller; calls in one stream
+ *   are ordered.  SV_ELAUNCH if the array's address cannot be obtained. */
+int sv_verify_window_noalloc(const void *target_logits, int64_t target_seq_stride,
+                             const void *draft_logits, int64_t draft_seq_stride, int dtype,
+                             const int32_t *draft_tokens, const int32_t *window_len,
+                             int32_t B, int32_t gamma, int32_t V,
+                             uint64_t seed, uint64_t tag, const uint64_t *seq_ids,
+                             const int64_t *base_pos,
+                             int32_t *n_accepted, int32_t *out_tokens,
+                             float *p_draft, float *q_draft, hipStream_t stream);
 
 /* sv_verify_window in two halves on the same workspace and arguments:
  *   part SV_PART_ROW_STATS     -- the streaming pass over every needed logits

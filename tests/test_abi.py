@@ -34,7 +34,7 @@ def test_single_hip_runtime_is_mapped():
 def test_version_and_error_strings():
     L = _lib.lib()
     assert L.sv_version() == 10000
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         assert L.sv_strerror(st)
     assert L.sv_strerror(-99) == b"unknown status"
 
@@ -120,6 +120,15 @@ def test_bad_host_arguments_return_status_without_device_work():
     assert L.sv_rollback(fake, fake, 4, 3, 8, 0, fake, 8, fake, 0, None) == -1
     assert L.sv_rollback(None, fake, 4, 3, 8, 1, fake, 8, fake, 0, None) == -1
     assert L.sv_probe_read(fake, 17, fake, None) == -1
+    # no-allocation window: host checks, and a call beyond the static scratch
+    assert L.sv_verify_window_noalloc(fake, 0, fake, 0, 5, fake, None, 1, 4, 100, 0, 0, None, None,
+                                      fake, fake, None, None, None) == -2
+    assert L.sv_verify_window_noalloc(fake, 0, fake, 0, 1, fake, None, 1, 65, 100, 0, 0, None, None,
+                                      fake, fake, None, None, None) == -1
+    need = L.sv_workspace_size(0, 4096, 64, 1 << 21, 1)
+    assert need > 8 << 20
+    assert L.sv_verify_window_noalloc(fake, 0, fake, 0, 1, fake, None, 4096, 64, 1 << 21, 0, 0, None, None,
+                                      fake, fake, None, None, None) == -6
 
 
 def test_binding_rejects_host_tensors_before_any_call():
