@@ -150,12 +150,15 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
   char *wsb = static_cast<char *>(workspace);
   float2 *part = reinterpret_cast<float2 *>(wsb + L.part_off);
   SampleJob *jobs = reinterpret_cast<SampleJob *>(wsb + L.jobs_off);
+  const DrawScratch ds{reinterpret_cast<float *>(wsb + L.spart_off), L.cmax,
+                       reinterpret_cast<int32_t *>(wsb + L.arrive_off)};
 
   RowSet rs{};
   rs.t = static_cast<const char *>(target_logits);
   rs.t_stride_bytes = target_seq_stride * eb;
   rs.d = static_cast<const char *>(draft_logits);
   rs.d_stride_bytes = draft_seq_stride * eb;
+  rs.arrive = ds.arrive;
   rs.B = B;
   rs.R_out = 2 * gamma + 1;
   rs.d_slot0 = gamma + 1;
@@ -192,9 +195,8 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
     launch_row_stats(dtype, false, all, part, stream);
   }
   if (!(parts & (kPartFinish | kEarlyExit))) return launch_status();
-  float *spart = reinterpret_cast<float *>(wsb + L.spart_off);
   if (!(parts & kEarlyExit)) {
-    launch_window_finish(dtype, A, B, spart, L.cmax, stream);
+    launch_window_finish(dtype, A, B, ds, stream);
     return launch_status();
   }
   // Position blocks of doubling width [0,1), [1,3), [3,7), ... up to the bonus
@@ -212,6 +214,7 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
     st.add_target(lo, hi);
     st.add_draft(lo, std::min(hi, static_cast<int>(gamma)));
     st.status = lo == 0 ? nullptr : status;
+    st.arrive = lo == 0 ? ds.arrive : nullptr;  // every sequence has workgroups in the first block
     launch_row_stats(dtype, false, st, part, stream);
     if (hi <= gamma) {
       launch_stage_decide(dtype, A, B, lo, hi, status, stream);
@@ -219,7 +222,7 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
       WindowArgs Af = A;
       Af.stage_lo = lo;
       Af.status = status;
-      launch_stage_finish(dtype, Af, B, spart, L.cmax, stream);
+      launch_stage_finish(dtype, Af, B, ds, stream);
     }
   }
   return launch_status();
@@ -356,9 +359,12 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
   SampleJob *jobs = reinterpret_cast<SampleJob *>(wsb + L.jobs_off);
 
   const int64_t seq_bytes = static_cast<int64_t>(N) * V * eb;
+  const DrawScratch ds{reinterpret_cast<float *>(wsb + L.spart_off), L.cmax,
+                       reinterpret_cast<int32_t *>(wsb + L.arrive_off)};
   RowSet rs{};
   rs.t = static_cast<const char *>(target_logits);
   rs.t_stride_bytes = seq_bytes;
+  rs.arrive = ds.arrive;
   rs.d = static_cast<const char *>(draft_logits);
   rs.d_stride_bytes = seq_bytes;
   rs.B = B;
@@ -405,7 +411,7 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
     return launch_status();
   }
   if (mode == SV_TREE_STOCHASTIC)
-    launch_tree_decide_draw(dtype, A, B, reinterpret_cast<float *>(wsb + L.spart_off), L.cmax, stream);
+    launch_tree_decide_draw(dtype, A, B, ds, stream);
   else
     launch_tree_decide(dtype, A, B, stream);
   return launch_status();
@@ -473,7 +479,8 @@ int sv_verify_window_lmhead(const void *hidden_target, const void *unembed_targe
   float *gath = reinterpret_cast<float *>(wsb + L.gath_off);
   int32_t *idx = reinterpret_cast<int32_t *>(wsb + L.idx_off);
   SampleJob *jobs = reinterpret_cast<SampleJob *>(wsb + L.jobs_off);
-  float *spart = reinterpret_cast<float *>(wsb + L.spart_off);
+  const DrawScratch ds{reinterpret_cast<float *>(wsb + L.spart_off), L.cmax,
+                       reinterpret_cast<int32_t *>(wsb + L.arrive_off)};
   float *rows_t = reinterpret_cast<float *>(wsb + L.rows_t_off);
   float *rows_d = reinterpret_cast<float *>(wsb + L.rows_d_off);
 
@@ -524,6 +531,7 @@ int sv_verify_window_lmhead(const void *hidden_target, const void *unembed_targe
   D.rows_d = rows_d;
   D.idx_t = idx;
   D.idx_d = idx + B;
+  D.arrive = ds.arrive;
   launch_lm_decide(D, B, stream);
 
   // pass 2: target row n and draft row n of every sequence, stored in float32
@@ -537,7 +545,7 @@ int sv_verify_window_lmhead(const void *hidden_target, const void *unembed_targe
   Sd.out = rows_d;
   launch_lm_gemm(LM_STORE, S, Sd, stream);
 
-  launch_tree_finish(SV_DT_F32, jobs, B, V, spart, L.cmax, stream);
+  launch_tree_finish(SV_DT_F32, jobs, B, V, ds, stream);
   return launch_status();
 }
 

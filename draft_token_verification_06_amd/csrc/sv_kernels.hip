@@ -6,9 +6,9 @@
 //   uniforms and finds the first rejection with a wavefront ballot --
 //   window_decide (in wave 0 of the draw), k_stage_decide (early exit, one
 //   block of positions), k_greedy_decide, k_tree_decide.
-// Sampling (k_finish, one 1024-thread workgroup per sequence; k_finish_part +
-//   k_finish_select for small batches): the one extra pass over the row of the
-//   first rejection (or the bonus row) keeps chunk sums of the weights in LDS,
+// Sampling (k_finish, one 1024-thread workgroup per sequence; k_finish_part,
+//   several per sequence, for small batches): the one extra pass over the row
+//   of the first rejection (or the bonus row) keeps chunk sums of the weights,
 //   then searches the chunk holding tau = v * Z.  The job comes from the window
 //   decision, from the last early-exit block's decision, or from the jobs array.
 // k_tree_walk: the lossless multi-candidate tree walk, one workgroup per
@@ -842,12 +842,16 @@ __global__ void __launch_bounds__(kFinThreads) k_finish(Args A, const SampleJob 
   if (tid == 0) *job.out_slot = y;
 }
 
-// Small batches, part 1, grid (B, G): workgroup g decides (redundantly, it is
-// cheap) and sums its share of the chunks into spart[b][c]; the g = 0
-// workgroup writes the window outputs and the job.
+// Small batches, grid (B, G): workgroup g decides (redundantly, it is cheap)
+// and sums its share of the chunks into spart[b][c]; the g = 0 workgroup
+// writes the window outputs and the job.  The last of the G workgroups of a
+// sequence to finish (a device-scope arrival counter; the launch before this
+// one zeroed it) reads all chunk sums and draws.  No workgroup waits for
+// another: the others just exit.
 template <int DT, int kSrc, typename Args = WindowArgs>
 __global__ void __launch_bounds__(kFinThreads) k_finish_part(Args A, SampleJob *__restrict__ jobs, int V,
-                                                            float *__restrict__ spart, int cmax) {
+                                                            float *__restrict__ spart, int cmax,
+                                                            int32_t *__restrict__ arrive) {
   const int b = blockIdx.x;
   const int g = blockIdx.y;
   const int G = gridDim.y;
@@ -855,6 +859,8 @@ __global__ void __launch_bounds__(kFinThreads) k_finish_part(Args A, SampleJob *
   __shared__ SampleJob s_job;
   __shared__ float s_wp[kFinMaxChunks * kFinWaves];
   __shared__ float s_cs[kFinMaxChunks];
+  __shared__ int s_last;
+  static_assert(kFinMaxChunks <= kFinThreads, "one chunk sum per thread in the draw");
   const bool decided = load_job<DT, kSrc>(A, jobs, b, g == 0, &s_job, tid);
   const SampleJob job = s_job;
   if (decided && g == 0 && tid == 0) jobs[b] = job;
@@ -869,26 +875,22 @@ __global__ void __launch_bounds__(kFinThreads) k_finish_part(Args A, SampleJob *
   __syncthreads();
   chunk_totals(s_wp, c0, c1, s_cs, tid);
   __syncthreads();
-  for (int c = c0 + tid; c < c1; c += kFinThreads) spart[static_cast<int64_t>(b) * cmax + c] = s_cs[c];
-}
-
-// Small batches, part 2, one workgroup per sequence: the draw from the chunk sums.
-template <int DT>
-__global__ void __launch_bounds__(kFinThreads) k_finish_select(const SampleJob *__restrict__ jobs, int V,
-                                                              const float *__restrict__ spart, int cmax) {
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  __shared__ float s_cs[kFinMaxChunks];
-  __shared__ float s_wp[kFinMaxChunks * kFinWaves];  // only for a draw without residual mass
-  static_assert(kFinMaxChunks <= kFinThreads, "one chunk sum per thread");
-  // the chunk sums travel with the job load (cmax >= C whatever the shift)
-  const float x = tid < cmax ? spart[static_cast<int64_t>(b) * cmax + tid] : 0.0f;
-  const SampleJob job = jobs[b];
-  if (job.mode == JOB_NONE) return;
-  const int h = job_shift(job, Elt<DT>::kBytes);
-  const bool vec = h >= 0;
-  const int C = vec ? finish_chunks<DT, true>(V, h) : finish_chunks<DT, false>(V, 0);
-  if (tid < C) s_cs[tid] = x;
+  // Hand-off without cache-wide write-backs: the chunk sums are stored and
+  // read back as device-scope atomics (written through to, and read from, the
+  // level the XCDs share), and every writer waits for its stores to complete
+  // before the workgroup's arrival is counted.
+  float *sp = spart + static_cast<int64_t>(b) * cmax;
+  for (int c = c0 + tid; c < c1; c += kFinThreads)
+    __hip_atomic_store(sp + c, s_cs[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(arrive + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (old + 1) % G == 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (tid < C) s_cs[tid] = __hip_atomic_load(sp + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   int y = vec ? draw_from_sums<DT, true>(job, V, C, h, s_cs, tid)
               : draw_from_sums<DT, false>(job, V, C, 0, s_cs, tid);
@@ -1129,34 +1131,32 @@ static int finish_split(int B, int V, int dtype) {
 }
 
 template <int DT, int kSrc, typename Args = WindowArgs>
-static void launch_finish_t(const Args &A, SampleJob *jobs, int B, int V, float *spart, int cmax,
-                            hipStream_t st) {
+static void launch_finish_t(const Args &A, SampleJob *jobs, int B, int V, const DrawScratch &ds, hipStream_t st) {
   const int G = finish_split(B, V, DT);
   if (G == 1) {
     hipLaunchKernelGGL((k_finish<DT, kSrc, Args>), dim3(B), dim3(kFinThreads), 0, st, A, jobs, V);
   } else {
-    hipLaunchKernelGGL((k_finish_part<DT, kSrc, Args>), dim3(B, G), dim3(kFinThreads), 0, st, A, jobs, V, spart,
-                       cmax);
-    hipLaunchKernelGGL(k_finish_select<DT>, dim3(B), dim3(kFinThreads), 0, st, jobs, V, spart, cmax);
+    hipLaunchKernelGGL((k_finish_part<DT, kSrc, Args>), dim3(B, G), dim3(kFinThreads), 0, st, A, jobs, V, ds.spart,
+                       ds.cmax, ds.arrive);
   }
 }
 
 template <int kSrc>
-static void launch_finish(int dtype, const WindowArgs &A, SampleJob *jobs, int B, int V, float *spart, int cmax,
+static void launch_finish(int dtype, const WindowArgs &A, SampleJob *jobs, int B, int V, const DrawScratch &ds,
                           hipStream_t st) {
   switch (dtype) {
-    case DT_BF16: launch_finish_t<DT_BF16, kSrc>(A, jobs, B, V, spart, cmax, st); break;
-    case DT_F16: launch_finish_t<DT_F16, kSrc>(A, jobs, B, V, spart, cmax, st); break;
-    default: launch_finish_t<DT_F32, kSrc>(A, jobs, B, V, spart, cmax, st); break;
+    case DT_BF16: launch_finish_t<DT_BF16, kSrc>(A, jobs, B, V, ds, st); break;
+    case DT_F16: launch_finish_t<DT_F16, kSrc>(A, jobs, B, V, ds, st); break;
+    default: launch_finish_t<DT_F32, kSrc>(A, jobs, B, V, ds, st); break;
   }
 }
 
-void launch_window_finish(int dtype, const WindowArgs &A, int B, float *spart, int cmax, hipStream_t st) {
-  launch_finish<SRC_WINDOW>(dtype, A, A.jobs, B, A.V, spart, cmax, st);
+void launch_window_finish(int dtype, const WindowArgs &A, int B, const DrawScratch &ds, hipStream_t st) {
+  launch_finish<SRC_WINDOW>(dtype, A, A.jobs, B, A.V, ds, st);
 }
 
-void launch_stage_finish(int dtype, const WindowArgs &A, int B, float *spart, int cmax, hipStream_t st) {
-  launch_finish<SRC_STAGE>(dtype, A, A.jobs, B, A.V, spart, cmax, st);
+void launch_stage_finish(int dtype, const WindowArgs &A, int B, const DrawScratch &ds, hipStream_t st) {
+  launch_finish<SRC_STAGE>(dtype, A, A.jobs, B, A.V, ds, st);
 }
 
 void launch_stage_decide(int dtype, const WindowArgs &A, int B, int lo, int hi, int32_t *status, hipStream_t st) {
@@ -1179,16 +1179,16 @@ void launch_tree_decide(int dtype, const TreeArgs &A, int B, hipStream_t st) {
   }
 }
 
-void launch_tree_finish(int dtype, SampleJob *jobs, int B, int V, float *spart, int cmax, hipStream_t st) {
+void launch_tree_finish(int dtype, SampleJob *jobs, int B, int V, const DrawScratch &ds, hipStream_t st) {
   const WindowArgs none{};
-  launch_finish<SRC_JOBS>(dtype, none, jobs, B, V, spart, cmax, st);
+  launch_finish<SRC_JOBS>(dtype, none, jobs, B, V, ds, st);
 }
 
-void launch_tree_decide_draw(int dtype, const TreeArgs &A, int B, float *spart, int cmax, hipStream_t st) {
+void launch_tree_decide_draw(int dtype, const TreeArgs &A, int B, const DrawScratch &ds, hipStream_t st) {
   switch (dtype) {
-    case DT_BF16: launch_finish_t<DT_BF16, SRC_TREE, TreeArgs>(A, A.jobs, B, A.V, spart, cmax, st); break;
-    case DT_F16: launch_finish_t<DT_F16, SRC_TREE, TreeArgs>(A, A.jobs, B, A.V, spart, cmax, st); break;
-    default: launch_finish_t<DT_F32, SRC_TREE, TreeArgs>(A, A.jobs, B, A.V, spart, cmax, st); break;
+    case DT_BF16: launch_finish_t<DT_BF16, SRC_TREE, TreeArgs>(A, A.jobs, B, A.V, ds, st); break;
+    case DT_F16: launch_finish_t<DT_F16, SRC_TREE, TreeArgs>(A, A.jobs, B, A.V, ds, st); break;
+    default: launch_finish_t<DT_F32, SRC_TREE, TreeArgs>(A, A.jobs, B, A.V, ds, st); break;
   }
 }
 

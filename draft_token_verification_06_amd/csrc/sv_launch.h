@@ -94,6 +94,7 @@ struct LmDecideArgs {
   SampleJob *jobs;
   const float *rows_t, *rows_d;  // where the second pass stores target / draft row n
   int32_t *idx_t, *idx_d;        // hidden rows of that pass
+  int32_t *arrive;               // arrival counters of the draw, zeroed here
 };
 
 // Launches the GEMMs of two problems (target rows, draft rows) as one grid.
@@ -102,14 +103,23 @@ int lm_gemm_blocks(int M, int V);
 void launch_lm_combine(const float2 *part, int NT, int M, float2 *stats, hipStream_t st);
 void launch_lm_decide(const LmDecideArgs &A, int B, hipStream_t st);
 
-void launch_window_finish(int dtype, const WindowArgs &A, int B, float *spart, int cmax, hipStream_t st);
+// Workspace of the split draw (several workgroups per sequence): chunk sums
+// spart [B][cmax] and one arrival counter per sequence, which the launch
+// before the draw zeroes.
+struct DrawScratch {
+  float *spart;
+  int cmax;
+  int32_t *arrive;
+};
+
+void launch_window_finish(int dtype, const WindowArgs &A, int B, const DrawScratch &ds, hipStream_t st);
 void launch_stage_decide(int dtype, const WindowArgs &A, int B, int lo, int hi, int32_t *status, hipStream_t st);
-void launch_stage_finish(int dtype, const WindowArgs &A, int B, float *spart, int cmax, hipStream_t st);
+void launch_stage_finish(int dtype, const WindowArgs &A, int B, const DrawScratch &ds, hipStream_t st);
 void launch_greedy_decide(const GreedyArgs &A, int B, hipStream_t st);
 void launch_tree_decide(int dtype, const TreeArgs &A, int B, hipStream_t st);
-void launch_tree_finish(int dtype, SampleJob *jobs, int B, int V, float *spart, int cmax, hipStream_t st);
+void launch_tree_finish(int dtype, SampleJob *jobs, int B, int V, const DrawScratch &ds, hipStream_t st);
 // Stochastic tree: the draw kernels decide each sequence themselves (no separate decision launch).
-void launch_tree_decide_draw(int dtype, const TreeArgs &A, int B, float *spart, int cmax, hipStream_t st);
+void launch_tree_decide_draw(int dtype, const TreeArgs &A, int B, const DrawScratch &ds, hipStream_t st);
 void launch_tree_walk(int dtype, const TreeArgs &A, int B, hipStream_t st);
 void launch_rollback(const RollbackArgs &A, int S, int stage, hipStream_t st);
 

@@ -293,6 +293,7 @@ __device__ __forceinline__ float lm_offset(float2 st) { return st.x * kLog2e + l
 __global__ void __launch_bounds__(kWave) k_lm_decide(LmDecideArgs A) {
   const int b = blockIdx.x;
   const int i = threadIdx.x;
+  if (i == 0) A.arrive[b] = 0;  // arrival counter of this sequence's draw
   const int g = A.gamma;
   int32_t *out = A.out_tokens + static_cast<int64_t>(b) * (g + 1);
   const int len = A.window_len ? A.window_len[b] : g;

@@ -92,7 +92,7 @@ struct Layout {
   RowPlan plan;
   int rows_per_seq;
   int cmax;  // chunk sums per sequence in the split draw
-  size_t part_off, jobs_off, spart_off, status_off, total;
+  size_t part_off, jobs_off, spart_off, status_off, arrive_off, total;
 };
 
 // op: 0 window, 1 greedy, 2 tree (n = gamma or N).
@@ -112,6 +112,8 @@ inline Layout make_layout(int op, int64_t B, int32_t n, int32_t V) {
   off = align256(off + sizeof(float) * static_cast<size_t>(B) * L.cmax);
   L.status_off = off;  // early-exit window: per-sequence status
   off = align256(off + (op == 0 ? sizeof(int32_t) * static_cast<size_t>(B) : 0));
+  L.arrive_off = off;  // split draw: per-sequence arrival counter
+  off = align256(off + (op == 1 ? 0 : sizeof(int32_t) * static_cast<size_t>(B)));
   L.total = off;
   return L;
 }
@@ -121,7 +123,7 @@ inline Layout make_layout(int op, int64_t B, int32_t n, int32_t V) {
 struct LmLayout {
   int NT;  // column tiles
   int cmax;
-  size_t part_off, stats_off, gath_off, idx_off, jobs_off, spart_off, rows_t_off, rows_d_off, total;
+  size_t part_off, stats_off, gath_off, idx_off, jobs_off, spart_off, arrive_off, rows_t_off, rows_d_off, total;
 };
 
 inline LmLayout make_lm_layout(int64_t B, int32_t gamma, int32_t V) {
@@ -142,6 +144,8 @@ inline LmLayout make_lm_layout(int64_t B, int32_t gamma, int32_t V) {
   off = align256(off + sizeof(SampleJob) * static_cast<size_t>(B));
   L.spart_off = off;
   off = align256(off + sizeof(float) * static_cast<size_t>(B) * L.cmax);
+  L.arrive_off = off;
+  off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
   L.rows_t_off = off;
   off = align256(off + sizeof(float) * static_cast<size_t>(B) * V);
   L.rows_d_off = off;

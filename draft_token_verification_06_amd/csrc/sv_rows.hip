@@ -176,6 +176,8 @@ __global__ void __launch_bounds__(kRowThreads) k_row_stats(RowSet rs, float2 *__
   const int j = static_cast<int>(rj % static_cast<uint32_t>(rs.R));
   const int64_t b = rj / static_cast<uint32_t>(rs.R);
 
+  // The arrival counters of the draw that follows start from zero.
+  if (rs.arrive && j == 0 && seg == 0 && threadIdx.x == 0) rs.arrive[b] = 0;
   if (rs.status && rs.status[b] != kSeqVerifying) return;
   int len = rs.gamma;
   if (rs.window_len) {

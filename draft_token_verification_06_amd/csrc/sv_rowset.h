@@ -33,6 +33,7 @@ struct RowSet {
   int64_t d_stride_bytes;
   const int32_t *window_len;      // window calls: rows past the window are skipped
   const int32_t *status;          // early exit: only sequences still verifying
+  int32_t *arrive;                // zeroed per sequence by its first workgroup (split draw)
   int32_t B, R;                   // sequences, listed rows per sequence
   int32_t R_out, d_slot0;         // row results per sequence, slot of draft row 0
   int32_t gamma;
