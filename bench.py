@@ -62,7 +62,7 @@ MAX_CPU_WORKERS = 16
 # each scaled by the same counter on the 1 GiB copy this script performs
 # (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000).  Valid for the kernel sources whose
 # hash is recorded; reported as null for any other build.
-PMC_TRAFFIC = {"kernel_sha": "bcfa064e0aa09846", "bytes": 1117003227}
+PMC_TRAFFIC = {"kernel_sha": "6584ea1e9f53f533", "bytes": 1117006512}
 
 
 def kernel_sha():
