@@ -545,6 +545,25 @@ def side_workloads(torch, sv, synth, dev):
             out[name]["us_same_inputs"] = ms1 * 1e3
     del b8
 
+    # One GPU's share of the B=256 workload sharded over 8 GPUs: by batch (B=32,
+    # no exchange) and by vocabulary (V/8 = 16032 columns; the two small
+    # all-gathers a vocabulary shard needs are not part of this).  Inputs
+    # rotate over 8 copies (1.1 GB), beyond the Infinity Cache.
+    for name, Bs, Vs in (("shard_batch_B32_g8_V128256_bf16", 32, 128256),
+                         ("shard_vocab_B256_g8_V16032_bf16", 256, 16032)):
+        copies = [synth.window_batch(Bs, GAMMA, Vs, "bf16", 3.0, 6.0, 1.06, seed=3000 + 10 * k, device=dev)
+                  for k in range(8)]
+        w = sv.workspace(sv.SV_OP_WINDOW, Bs, GAMMA, Vs, torch.bfloat16, dev)
+        nbytes = Bs * (2 * GAMMA + 1) * Vs * 2
+
+        def call(c=iter(range(10 ** 9))):
+            x = copies[next(c) % len(copies)]
+            sv.verify_window(x["target"], x["draft"], x["tokens"], ws=w)
+        ms = event_time_ms(torch, call, reps)
+        out[name] = {"us": ms * 1e3, "GBps": nbytes / (ms * 1e-3) / 1e9, "input_copies": len(copies),
+                     "verified_drafts_per_s": Bs * GAMMA / (ms * 1e-3)}
+        del copies, w
+
     # the B=8 window captured once in a HIP graph and replayed (launch-bound)
     d = synth.window_batch(8, 8, 128256, "bf16", 3.0, 6.0, 1.0, seed=1002, device=dev)
     w = sv.workspace(sv.SV_OP_WINDOW, 8, 8, 128256, torch.bfloat16, dev)
