@@ -6,7 +6,8 @@
 //
 // GEMM: C[M x V] = A[M x K] * W[V x K]^T, bf16 inputs, float32 accumulation in
 // v_mfma_f32_32x32x16_bf16.  Block tile 256 x 256, K step 64, 8 waves of 64 x
-// 128 (4 along M, 2 along V), double-buffered LDS, one barrier per K step.
+// 128 (4 along M, 2 along V), double-buffered LDS, one barrier per K step; a
+// tile's global loads are issued a whole K step before they are stored to LDS.
 // Operand layout of the 32x32x16 instruction (checked on the device): lane l
 // supplies A[l % 32][8 (l / 32) + j] and W-row (l % 32) at the same k, j < 8;
 // accumulator register r of lane l is C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
@@ -123,20 +124,20 @@ __device__ __forceinline__ void lm_gemm_tile(const LmGemmArgs &P, int L) {
       *reinterpret_cast<uint4 *>(lds + (st) * kStageElems + woff[j]) = rw[j];
 
   const int nk = P.K / kBK;
+  // A tile's loads go out right after the previous tile left the registers
+  // for LDS, so they have a whole K step to land before their own stash
+  // (issued at the top of the step they had half a step: 4.25 -> 3.96 ms per
+  // fused call, same box, bit-identical outputs).
   SV_LM_FETCH(0)
   SV_LM_STASH(0)
+  if (nk > 1) {
+    SV_LM_FETCH(kBK)
+  }
   __syncthreads();
-#ifndef SV_LM_PIPE
-#define SV_LM_PIPE 1
-#endif
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
-    if (kt + 1 < nk) {
-      SV_LM_FETCH((kt + 1) * kBK)
-    }
     const uint16_t *sa = lds + st * kStageElems + (wm * kWaveM + c32) * kLdsRow + 8 * half;
     const uint16_t *sw = lds + st * kStageElems + kBM * kLdsRow + (wn * 128 + c32) * kLdsRow + 8 * half;
-#if SV_LM_PIPE
     // operands of K sub-step ks + 1 are read while sub-step ks multiplies; the
     // next tile goes to the other LDS stage in the middle of the step
     bf16x8_t a[2][kMT], w[2][4];
@@ -162,28 +163,11 @@ __device__ __forceinline__ void lm_gemm_tile(const LmGemmArgs &P, int L) {
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mt], w[cur][nt], acc[mt][nt], 0, 0, 0);
       if (ks == (kBK / 16) / 2 - 1 && kt + 1 < nk) {
         SV_LM_STASH(st ^ 1)
+        if (kt + 2 < nk) {
+          SV_LM_FETCH((kt + 2) * kBK)
+        }
       }
     }
-#else
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8_t a[kMT], w[4];
-#pragma unroll
-      for (int mt = 0; mt < kMT; ++mt)
-        a[mt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sa + mt * 32 * kLdsRow + ks * 16));
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        w[nt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sw + nt * 32 * kLdsRow + ks * 16));
-#pragma unroll
-      for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], w[nt], acc[mt][nt], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-      SV_LM_STASH(st ^ 1)
-    }
-#endif
     __syncthreads();
   }
 #undef SV_LM_FETCH
