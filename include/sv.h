@@ -147,7 +147,10 @@ int sv_verify_window_noalloc(const void *target_logits, int64_t target_seq_strid
  *                                 residual / bonus draw.
  * Running ROW_STATS then DECIDE_SAMPLE on one stream equals one
  * sv_verify_window call bit for bit.  Lets a caller overlap the streaming pass
- * with other work or time it on its own. */
+ * with other work or time it on its own.  DECIDE_SAMPLE reads what ROW_STATS
+ * left in the workspace (row results, and the draw's zeroed arrival counters),
+ * so it must follow a ROW_STATS on the same workspace and arguments; it may be
+ * repeated after one. */
 #define SV_PART_ROW_STATS 1
 #define SV_PART_DECIDE_SAMPLE 2
 int sv_verify_window_part(int part, const void *target_logits, int64_t target_seq_stride,
