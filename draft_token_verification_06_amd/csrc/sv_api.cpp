@@ -13,7 +13,7 @@ using namespace sv;
 
 namespace {
 
-constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kVersion = 10100;  // 1.1.0
 
 // The row list of a launch holds a full window's rows and a tree's target rows
 // plus its internal draft rows.

@@ -33,7 +33,7 @@ def test_single_hip_runtime_is_mapped():
 
 def test_version_and_error_strings():
     L = _lib.lib()
-    assert L.sv_version() == 10000
+    assert L.sv_version() == 10100
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert L.sv_strerror(st)
     assert L.sv_strerror(-99) == b"unknown status"

@@ -61,3 +61,16 @@ def test_greedy_and_early_exit_graph_replays():
     _replays_match(lambda: sv.verify_window(d["target"], d["draft"], d["tokens"], seed=1, ws=ws, out=out,
                                             early_exit=True),
                    [out.n_accepted, out.out_tokens])
+
+
+def test_noalloc_window_graph_replays():
+    """The no-allocation window (its workspace is the library's static device
+    array) captured and replayed: every replay equals the eager result."""
+    print("graph no-alloc window", flush=True)
+    d = synth.window_batch(8, 8, 128256, "bf16", 3.0, 6.0, 1.0, seed=1003, device=DEV)
+    out = sv.WindowResult(torch.empty(8, dtype=torch.int32, device=DEV),
+                          torch.empty(8, 9, dtype=torch.int32, device=DEV),
+                          torch.empty(8, 8, dtype=torch.float32, device=DEV),
+                          torch.empty(8, 8, dtype=torch.float32, device=DEV))
+    _replays_match(lambda: sv.verify_window_noalloc(d["target"], d["draft"], d["tokens"], seed=4, out=out),
+                   [out.n_accepted, out.out_tokens, out.p_draft, out.q_draft])
