@@ -8,11 +8,17 @@
 // v_mfma_f32_32x32x16_bf16.  Block tile 256 x 256, K step 64, 8 waves of 64 x
 // 128 (4 along M, 2 along V), double-buffered LDS, one barrier per K step; a
 // tile's global loads are issued a whole K step before they are stored to LDS.
+// The K loop's issue order is fixed by hand: every MFMA is followed by its
+// share of LDS reads, LDS stores and global loads, so the two waves of a SIMD
+// keep the matrix core fed while the LDS traffic (the binding resource at
+// this wave tile) flows.
 // Operand layout of the 32x32x16 instruction (checked on the device): lane l
 // supplies A[l % 32][8 (l / 32) + j] and W-row (l % 32) at the same k, j < 8;
 // accumulator register r of lane l is C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "sv_device.h"
 #include "sv_launch.h"
@@ -23,19 +29,10 @@ namespace sv {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-#ifndef SV_LM_BM
-#define SV_LM_BM 256
-#endif
-#ifndef SV_LM_BK
-#define SV_LM_BK 64
-#endif
-#ifndef SV_LM_WAVEM
-#define SV_LM_WAVEM 64
-#endif
-constexpr int kBM = SV_LM_BM;              // rows per block
+constexpr int kBM = 256;                   // rows per block
 constexpr int kBN = kLmBN;                 // 2 waves along V, 128 columns each
-constexpr int kBK = SV_LM_BK;
-constexpr int kWaveM = SV_LM_WAVEM;        // rows per wave: kBM / kWaveM waves along M
+constexpr int kBK = 64;                    // K step: four MFMA sub-steps of 16
+constexpr int kWaveM = 64;                 // rows per wave: kBM / kWaveM waves along M
 constexpr int kMT = kWaveM / 32;           // 32-row accumulator tiles per wave
 constexpr int kWavesM = kBM / kWaveM;
 constexpr int kGemmThreads = 64 * kWavesM * 2;
@@ -58,6 +55,19 @@ __device__ __forceinline__ bool lm_tile(int L, int RB, int NT, int *rb, int *ct)
   return *ct < NT;
 }
 
+// Lane exchanges within a wave: a DPP move (kCtrl: quad permutation or row
+// rotation, within rows of 16 lanes) and lane l ^ 16 within each half-wave.
+template <int kCtrl>
+__device__ __forceinline__ float lm_dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, true));
+}
+// Larger of two floats that are never NaN here, without canonicalising
+// operands that come from lane exchanges.
+__device__ __forceinline__ float lm_max(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float lm_swap16(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+
 // One 256 x 256 output tile of problem P; L is the block's index within P.
 template <int kMode>
 __device__ __forceinline__ void lm_gemm_tile(const LmGemmArgs &P, int L) {
@@ -65,6 +75,7 @@ __device__ __forceinline__ void lm_gemm_tile(const LmGemmArgs &P, int L) {
   uint16_t *lds = reinterpret_cast<uint16_t *>(lds_raw);
   __shared__ float2 s_red[2][kBM];
   __shared__ int s_tok[kBM];
+  __shared__ float s_gath[kBM + 64];
   int rb, ct;
   if (!lm_tile(L, P.RB, P.NT, &rb, &ct)) return;
   const int tid = threadIdx.x;
@@ -114,64 +125,95 @@ __device__ __forceinline__ void lm_gemm_tile(const LmGemmArgs &P, int L) {
   // Rows past M (A) or V (W) load row 0, in bounds; their products land in
   // accumulator rows that are never stored and columns the epilogues mask.
   uint4 ra[kLoadsA], rw[kLoadsW];
-#define SV_LM_FETCH(k0)                                                                   \
-  _Pragma("unroll") for (int j = 0; j < kLoadsA; ++j) ra[j] = load_vec(asrc[j] + (k0) / 8); \
-  _Pragma("unroll") for (int j = 0; j < kLoadsW; ++j) rw[j] = load_vec(wsrc[j] + (k0) / 8);
-#define SV_LM_STASH(st)                                                                              \
-  _Pragma("unroll") for (int j = 0; j < kLoadsA; ++j)                                                \
-      *reinterpret_cast<uint4 *>(lds + (st) * kStageElems + aoff[j]) = ra[j];                        \
-  _Pragma("unroll") for (int j = 0; j < kLoadsW; ++j)                                                \
-      *reinterpret_cast<uint4 *>(lds + (st) * kStageElems + woff[j]) = rw[j];
-
+  bf16x8_t a[2][kMT], w[2][4];  // operand fragments of two sub-steps
   const int nk = P.K / kBK;
-  // A tile's loads go out right after the previous tile left the registers
-  // for LDS, so they have a whole K step to land before their own stash
-  // (issued at the top of the step they had half a step: 4.25 -> 3.96 ms per
-  // fused call, same box, bit-identical outputs).
-  SV_LM_FETCH(0)
-  SV_LM_STASH(0)
-  if (nk > 1) {
-    SV_LM_FETCH(kBK)
+  // Load item j of a tile (j < kLoadsA: A chunk, else W chunk) at K offset
+  // k0 into the staging registers, store it to LDS stage st, and read
+  // fragment f of sub-step ks of stage st (f = 0: A tile 0, 1..4: W tiles
+  // 0..3, 5..: A tiles 1..) into slot.
+#define SV_LM_LOAD1(j, k0)                                            \
+  {                                                                   \
+    if ((j) < kLoadsA)                                                \
+      ra[j] = load_vec(asrc[j] + (k0) / 8);                           \
+    else                                                              \
+      rw[(j) - kLoadsA] = load_vec(wsrc[(j) - kLoadsA] + (k0) / 8);   \
   }
+#define SV_LM_STORE1(j, st)                                                                       \
+  {                                                                                               \
+    if ((j) < kLoadsA)                                                                            \
+      *reinterpret_cast<uint4 *>(lds + (st) * kStageElems + aoff[j]) = ra[j];                     \
+    else                                                                                          \
+      *reinterpret_cast<uint4 *>(lds + (st) * kStageElems + woff[(j) - kLoadsA]) = rw[(j) - kLoadsA]; \
+  }
+#define SV_LM_FRAG(slot, st, ks, f)                                                                        \
+  {                                                                                                        \
+    const uint16_t *sa_ = lds + (st) * kStageElems + (wm * kWaveM + c32) * kLdsRow + 8 * half + (ks) * 16; \
+    const uint16_t *sw_ =                                                                                  \
+        lds + (st) * kStageElems + kBM * kLdsRow + (wn * 128 + c32) * kLdsRow + 8 * half + (ks) * 16;      \
+    if ((f) == 0)                                                                                          \
+      a[slot][0] = as_bf16x8(*reinterpret_cast<const uint4 *>(sa_));                                       \
+    else if ((f) <= 4)                                                                                     \
+      w[slot][(f) - 1] = as_bf16x8(*reinterpret_cast<const uint4 *>(sw_ + ((f) - 1) * 32 * kLdsRow));      \
+    else                                                                                                   \
+      a[slot][(f) - 4] = as_bf16x8(*reinterpret_cast<const uint4 *>(sa_ + ((f) - 4) * 32 * kLdsRow));      \
+  }
+  // One sub-step: the MFMAs of slot cur, in a fixed issue order.  The reads
+  // of the next sub-step's fragments (stage st_r, sub-step ks_r, into slot
+  // nxt) go out two after each of the first MFMAs; with tile set, each MFMA
+  // is also followed by its share of the tile hand-over: store an item of the
+  // tile fetched a step earlier to stage st_w, then fetch the same item two
+  // steps ahead (K offset k0).  The fences keep the scheduler from moving
+  // anything across them.
+#define SV_LM_SUBSTEP(cur, nxt, st_r, ks_r, tile, st_w, k0)                                                   \
+  _Pragma("unroll") for (int i_ = 0; i_ < kSubMfma; ++i_) {                                                   \
+    acc[i_ / 4][i_ % 4] =                                                                                     \
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i_ / 4], w[cur][i_ % 4], acc[i_ / 4][i_ % 4], 0, 0, 0); \
+    _Pragma("unroll") for (int f_ = 2 * i_; f_ < 2 * i_ + 2; ++f_) if (f_ < kSubFrags)                        \
+        SV_LM_FRAG(nxt, st_r, ks_r, f_)                                                                       \
+    if (tile)                                                                                                 \
+      _Pragma("unroll") for (int j_ = i_ * kTileItems / kSubMfma; j_ < (i_ + 1) * kTileItems / kSubMfma; ++j_) { \
+        SV_LM_STORE1(j_, st_w)                                                                                \
+        SV_LM_LOAD1(j_, k0)                                                                                   \
+      }                                                                                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                                        \
+  }
+  constexpr int kSubMfma = kMT * 4, kSubFrags = kMT + 4, kTileItems = kLoadsA + kLoadsW;
+  static_assert(kSubFrags <= 2 * kSubMfma && kTileItems <= 2 * kSubMfma, "a sub-step carries the hand-over");
+
+  // Prologue: tile 0 to stage 0, tile 1 in the registers, the first fragments.
+#pragma unroll
+  for (int j = 0; j < kTileItems; ++j) SV_LM_LOAD1(j, 0)
+#pragma unroll
+  for (int j = 0; j < kTileItems; ++j) SV_LM_STORE1(j, 0)
+#pragma unroll
+  for (int j = 0; j < kTileItems; ++j) SV_LM_LOAD1(j, (nk > 1 ? kBK : 0))
   __syncthreads();
+#pragma unroll
+  for (int f = 0; f < kSubFrags; ++f) SV_LM_FRAG(0, 0, 0, f)
+  __builtin_amdgcn_sched_barrier(0);
+  // K step kt multiplies stage st = kt & 1 in four sub-steps of 16.  Sub-step
+  // 1 stores the tile of step kt + 1 (fetched during step kt - 1) to stage
+  // st ^ 1 and fetches the tile of step kt + 2.  One barrier, after sub-step
+  // 2, separates every wave's last read of stage st and its stores to stage
+  // st ^ 1 from the reads of stage st ^ 1 and, one step later, from the
+  // stores that overwrite stage st; sub-step 3 multiplies from registers and
+  // meanwhile reads the next stage's first fragments.  The last steps store
+  // and fetch tiles nobody reads (K offsets clamped in range), so the loop
+  // body has no branches.
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
-    const uint16_t *sa = lds + st * kStageElems + (wm * kWaveM + c32) * kLdsRow + 8 * half;
-    const uint16_t *sw = lds + st * kStageElems + kBM * kLdsRow + (wn * 128 + c32) * kLdsRow + 8 * half;
-    // operands of K sub-step ks + 1 are read while sub-step ks multiplies; the
-    // next tile goes to the other LDS stage in the middle of the step
-    bf16x8_t a[2][kMT], w[2][4];
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) a[0][mt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sa + mt * 32 * kLdsRow));
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) w[0][nt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sw + nt * 32 * kLdsRow));
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int cur = ks & 1, nxt = cur ^ 1;
-      if (ks + 1 < kBK / 16) {
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt)
-          a[nxt][mt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sa + mt * 32 * kLdsRow + (ks + 1) * 16));
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          w[nxt][nt] = as_bf16x8(*reinterpret_cast<const uint4 *>(sw + nt * 32 * kLdsRow + (ks + 1) * 16));
-      }
-#pragma unroll
-      for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mt], w[cur][nt], acc[mt][nt], 0, 0, 0);
-      if (ks == (kBK / 16) / 2 - 1 && kt + 1 < nk) {
-        SV_LM_STASH(st ^ 1)
-        if (kt + 2 < nk) {
-          SV_LM_FETCH((kt + 2) * kBK)
-        }
-      }
-    }
+    const int kf = min(kt + 2, nk - 1) * kBK;
+    SV_LM_SUBSTEP(0, 1, st, 1, false, 0, 0)
+    SV_LM_SUBSTEP(1, 0, st, 2, true, st ^ 1, kf)
+    SV_LM_SUBSTEP(0, 1, st, 3, false, 0, 0)
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    SV_LM_SUBSTEP(1, 0, st ^ 1, 0, false, 0, 0)
   }
-#undef SV_LM_FETCH
-#undef SV_LM_STASH
+#undef SV_LM_SUBSTEP
+#undef SV_LM_FRAG
+#undef SV_LM_STORE1
+#undef SV_LM_LOAD1
 
   if (kMode == LM_STORE) {
 #pragma unroll
@@ -192,44 +234,75 @@ __device__ __forceinline__ void lm_gemm_tile(const LmGemmArgs &P, int L) {
 
   // Row statistics of this wave's 128 columns: max, then sum of exp(x - max)
   // (the same 2^(x log2e - m log2e) form as the streaming row pass), across
-  // the 32 lanes of each half-wave; the draft token's logit is picked up by
-  // the lane holding its column.
+  // the 32 lanes of each half-wave: within each row of 16 lanes by DPP
+  // (swap neighbours, swap pairs, rotate by 4 and by 8), then across the two
+  // rows of the half by a swizzle.  Lane j of a half keeps the result of the
+  // half's j-th row (and row j + 32 with four row tiles), so the loop has no
+  // branches and one LDS store per lane ends it.  The lane holding a row's
+  // draft-token column leaves that logit in s_gath (other lanes write a
+  // scratch slot of their own).
+  const bool full = col0 + kBN <= P.V;
+  const int cbase = col0 + wn * 128 + c32;
+  constexpr int kKeep = kMT / 2;
+  float keep_m[kKeep], keep_s[kKeep];
+#pragma unroll
+  for (int q = 0; q < kKeep; ++q) {
+    keep_m[q] = kNegInf;
+    keep_s[q] = 0.0f;
+  }
+  auto rows = [&](auto masked) {
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int rl = wm * kWaveM + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
       float v[4];
-      float m = kNegInf;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int col = col0 + wn * 128 + nt * 32 + c32;
-        v[nt] = col < P.V ? acc[mt][nt][r] : kNegInf;
-        m = fmaxf(m, v[nt]);
-      }
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+      for (int nt = 0; nt < 4; ++nt)
+        v[nt] = (!decltype(masked)::value || cbase + nt * 32 < P.V) ? acc[mt][nt][r] : kNegInf;
+      float m = lm_max(lm_max(v[0], v[1]), lm_max(v[2], v[3]));
+      m = lm_max(m, lm_dpp<0xB1>(m));
+      m = lm_max(m, lm_dpp<0x4E>(m));
+      m = lm_max(m, lm_dpp<0x124>(m));
+      m = lm_max(m, lm_dpp<0x128>(m));
+      m = lm_max(m, lm_swap16(m));
+      const float ml = m != kNegInf ? m * kLog2e : 0.0f;
       float s = 0.0f;
-      if (m != kNegInf) {
-        const float ml = m * kLog2e;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) s += exp_shift(v[nt], ml);
-      }
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) s += __shfl_xor(s, off);
-      const int x = s_tok[rl];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int col = col0 + wn * 128 + nt * 32 + c32;
-        if (col == x) P.gath[row0 + rl] = acc[mt][nt][r];
-      }
-      if (c32 == 0) s_red[wn][rl] = make_float2(m, s);
+      for (int nt = 0; nt < 4; ++nt) s += exp_shift(v[nt], ml);
+      s += lm_dpp<0xB1>(s);
+      s += lm_dpp<0x4E>(s);
+      s += lm_dpp<0x124>(s);
+      s += lm_dpp<0x128>(s);
+      s += lm_swap16(s);
+      const int j = mt * 16 + r;
+      keep_m[j / 32] = c32 == j % 32 ? m : keep_m[j / 32];
+      keep_s[j / 32] = c32 == j % 32 ? s : keep_s[j / 32];
+      const int d = s_tok[rl] - cbase;
+      float g = acc[mt][0][r];
+      g = d == 32 ? acc[mt][1][r] : g;
+      g = d == 64 ? acc[mt][2][r] : g;
+      g = d == 96 ? acc[mt][3][r] : g;
+      const bool hit = d >= 0 && d < 128 && (d & 31) == 0;
+      s_gath[hit ? rl : kBM + lane] = g;
     }
+  };
+  if (full)  // every column of the tile lies inside the vocabulary
+    rows(std::false_type{});
+  else
+    rows(std::true_type{});
+#pragma unroll
+  for (int q = 0; q < kKeep; ++q) {
+    const int j = 32 * q + c32, mt = j / 16, r = j % 16;
+    s_red[wn][wm * kWaveM + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3)] = make_float2(keep_m[q], keep_s[q]);
+  }
   __syncthreads();
   if (tid < kBM && row0 + tid < P.M) {
     const float2 p0 = s_red[0][tid], p1 = s_red[1][tid];
     const MaxSum c = combine(MaxSum{p0.x, p0.y}, MaxSum{p1.x, p1.y});
     P.part[static_cast<int64_t>(row0 + tid) * P.NT + ct] = make_float2(c.m, c.s);
+    const int x = s_tok[tid];
+    if (x >= col0 && x < col0 + kBN) P.gath[row0 + tid] = s_gath[tid];
   }
 }
 
