@@ -44,6 +44,9 @@ def test_margin_rule_looks_only_at_the_point_of_divergence():
 def test_pooled_oracle_baseline_counts_a_planted_mismatch(monkeypatch):
     B = 3
     monkeypatch.setattr(bench, "B", B)
+    # a second, timing-only round of the four calls
+    monkeypatch.setattr(bench, "CPU_SAMPLE_SECONDS", 1e9)
+    monkeypatch.setattr(bench, "CPU_SAMPLE_MAX_ROUNDS", 2)
     data = [synth.window_config5(a, B=B, seed=1005 + k, device="cpu") for k, a in enumerate(bench.ALPHAS)]
     ref = []
     for d in data:
@@ -66,6 +69,8 @@ def test_pooled_oracle_baseline_counts_a_planted_mismatch(monkeypatch):
     assert base["cores"] == 2 and base["kind"] == "oracle" and base["value"] > 0
     assert sorted(base["full_call_wall_s"]) == sorted(str(a) for a in bench.ALPHAS)
     assert base["single_core_ms_per_sequence"] > 0
+    assert base["calls"] == 2 * len(bench.ALPHAS) and base["sample"].startswith("2 round(s)")
+    assert 0 < base["cpu_seconds"] and abs(base["value"] - B * bench.GAMMA * base["calls"] / base["seconds"]) < 1e-6 * base["value"]
     assert len(parity["beta"]) == len(bench.ALPHAS)
     for st in parity["beta"]:
         assert 1.0 <= st["exact_expected_emitted"] <= bench.GAMMA + 1 and 0.0 < st["mean_alpha"] < 1.0
