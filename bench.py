@@ -49,7 +49,7 @@ KERNEL_SOURCES = ("sv_rows.hip", "sv_device.h", "sv_rowset.h")
 
 # Launches per HIP-event span of the kernel-level timings (row pass, draw,
 # whole call, per acceptance level): fixed, whatever --steps asks for, so the
-# roofline figure does not depend on the driver's flags.
+# roofline figure does not depend on the command-line step count.
 EVENT_SPAN = 1000
 ALPHA_SPAN = 500
 # Worker processes of the oracle baseline: the host's cores, at most 16 (the
