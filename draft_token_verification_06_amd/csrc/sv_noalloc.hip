@@ -47,12 +47,15 @@ extern "C" int sv_verify_window_noalloc(const void *target_logits, int64_t targe
                                         const int64_t *base_pos,
                                         int32_t *n_accepted, int32_t *out_tokens,
                                         float *p_draft, float *q_draft, hipStream_t stream) {
-  const size_t need = sv_workspace_size(SV_OP_WINDOW, B, gamma, V, dtype);
-  if (need == 0) {
-    if (dtype != SV_DT_F32 && dtype != SV_DT_BF16 && dtype != SV_DT_F16) return SV_EDTYPE;
-    return SV_EINVAL;
-  }
-  if (need > SV_SCRATCH_BYTES) return SV_ESCRATCH;
+  // Argument errors come first, whatever the state of the device: the
+  // workspace call checks every argument before its workspace, so without one
+  // it reports either an argument error or only the missing workspace, and
+  // enqueues nothing either way.
+  const int args = sv_verify_window(target_logits, target_seq_stride, draft_logits, draft_seq_stride, dtype,
+                                    draft_tokens, window_len, B, gamma, V, seed, tag, seq_ids, base_pos, n_accepted,
+                                    out_tokens, p_draft, q_draft, nullptr, 0, stream);
+  if (args != SV_EWORKSPACE) return args;
+  if (sv_workspace_size(SV_OP_WINDOW, B, gamma, V, dtype) > SV_SCRATCH_BYTES) return SV_ESCRATCH;
   void *ws = scratch_ptr();
   if (!ws) return SV_ELAUNCH;
   return sv_verify_window(target_logits, target_seq_stride, draft_logits, draft_seq_stride, dtype, draft_tokens,

@@ -130,7 +130,8 @@ int sv_verify_window(const void *target_logits, int64_t target_seq_stride,
  *   Every call on one GPU shares that array and no state survives between
  *   calls, so calls that overlap on one GPU (different streams, or host
  *   threads) race and must be serialised by the caller; calls in one stream
- *   are ordered.  SV_ELAUNCH if the array's address cannot be obtained. */
+ *   are ordered.  Argument errors (SV_EDTYPE, SV_EINVAL) are reported first,
+ *   then SV_ESCRATCH; SV_ELAUNCH if the array's address cannot be obtained. */
 int sv_verify_window_noalloc(const void *target_logits, int64_t target_seq_stride,
                              const void *draft_logits, int64_t draft_seq_stride, int dtype,
                              const int32_t *draft_tokens, const int32_t *window_len,
