@@ -66,3 +66,22 @@ def test_lmhead_is_deterministic():
     b = _run(d, seed=2)
     assert torch.equal(a.n_accepted, b.n_accepted) and torch.equal(a.out_tokens, b.out_tokens)
     assert torch.equal(a.p_draft, b.p_draft) and torch.equal(a.q_draft, b.q_draft)
+
+
+@pytest.mark.parametrize("k", range(6))
+def test_random_lmhead_configuration(k):
+    """Random shapes against the oracle: B, gamma, a vocabulary that often
+    leaves a ragged last column tile, and hidden widths of one to eight K
+    steps (the GEMM's first and last steps load clamped tiles)."""
+    rng = np.random.default_rng(9100 + k)
+    B = int(rng.choice([1, 3, 17, 40]))
+    gamma = int(rng.choice([1, 3, 8, 13]))
+    V = int(rng.choice([7, 257, 1000, 4099]))
+    Ht = 64 * int(rng.integers(1, 9))
+    Hd = 64 * int(rng.integers(1, Ht // 64 + 1))
+    seed = int(rng.integers(0, 1000))
+    print("lmhead random", k, B, gamma, V, Ht, Hd, flush=True)
+    d = synth.lmhead_batch(B, gamma, V, Ht, Hd, seed=seed, device=DEV)
+    res = _run(d, seed=seed)
+    n, m = check_lmhead(d, res, seed=seed)
+    assert m <= 1
