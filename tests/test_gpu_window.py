@@ -159,7 +159,7 @@ def test_one_hot_draws_at_slot_wave_and_chunk_boundaries(dtype):
     and the residual draw (a draft with all mass elsewhere) must return k, for
     k at the first and last slot of a thread, of a wave's range and of a
     chunk, and at the vocabulary's end.  B >= 256 takes the one-workgroup draw,
-    B = 8 the split draw and its select kernel."""
+    B = 8 the split draw, whose last-arriving workgroup searches the chunk sums."""
     V = 3 * 8192 + 517
     epv = 8 if dtype == "bf16" else 4  # elements per 16-byte slot
     chunk = 1024 * epv
@@ -255,7 +255,8 @@ def test_rejected_draft_without_residual_mass_draws_from_p(B, dtype, V):
     """A draft with p(x) = q(x) = 0 (masked in both rows) is rejected; when the
     two rows are otherwise identical the residual max(0, p - q) has no mass
     and the token is drawn from p, as in the oracle.  B = 3 takes the split
-    draw (the select kernel draws from p), B = 256 the one-workgroup draw."""
+    draw (its last-arriving workgroup draws from p), B = 256 the one-workgroup
+    draw."""
     gamma = 3
     _say("no residual mass", B, dtype, V)
     d = synth.window_batch(B, gamma, V, dtype, target_sd=2.0, boost=3.0, sigma=0.5, seed=44,
