@@ -1,0 +1,72 @@
+"""Chi-square pin of the HIP library's multi-candidate tree walk at V = 32000
+(the LLaMA-2 vocabulary), float32 logits: the first emitted token of every walk
+follows the target's law at the root.
+
+The walk is the multi-round scheme of SpecInfer, which the PipeSpec and CLaSp
+review pages cite by title ("tree-based speculative inference and
+verification"): sibling tokens drawn i.i.d. from the parent's draft row are
+tried in turn against the residual left by the rejected ones, and the output
+keeps the target's distribution.  Here the tree is a root with four children
+(every child's token drawn from the root's draft softmax), so the first token
+is an accepted child or the draw from the root's residual after four
+rejections; either way its law is p_root.  10^5 walks: 100 calls of 1000
+sequences, each with its own sequence id (so its own Philox uniforms) and
+its own four child tokens.  The expected law comes from scipy's softmax of
+the float32 rows the library reads; bins and threshold (10^-3) as in the
+window's pins at this size.  Power: the same statistic rejects q_root."""
+import numpy as np
+import pytest
+import torch
+from scipy.special import softmax as sp_softmax
+
+import draft_token_verification_06_amd as sv
+from test_oracle_chi2_large_vocab import THRESHOLD, _bins, _pvalue
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+V, CHILDREN = 32000, 4
+CALLS, B = 100, 1000
+
+
+def _rows():
+    rng = np.random.default_rng(4032000)
+    N = 1 + CHILDREN
+    T = rng.normal(0.0, 2.0, (N, V)).astype(np.float32)
+    D = (T.astype(np.float64) + rng.normal(0.0, 1.0, (N, V))).astype(np.float32)
+    return T, D
+
+
+def test_gpu_walk_first_token_follows_p_root():
+    print("GPU walk chi-square: 100 calls x 1000 trees, V=32000", flush=True)
+    T, D = _rows()
+    p0 = sp_softmax(T[0].astype(np.float64))
+    q0 = sp_softmax(D[0].astype(np.float64))
+    cq = np.cumsum(q0)
+    parent = [-1] + [0] * CHILDREN
+    N = len(parent)
+    target = torch.from_numpy(T).to(DEV)[None].expand(B, N, V).contiguous()
+    draft = torch.from_numpy(D).to(DEV)[None].expand(B, N, V).contiguous()
+    ws = sv.workspace(sv.SV_OP_TREE, B, N, V, torch.float32, DEV)
+    rng = np.random.default_rng(55)
+    first, depth = [], []
+    for c in range(CALLS):
+        u = rng.random((B, CHILDREN))
+        kids = np.minimum(V - 1, np.searchsorted(cq, u * cq[-1], side="right")).astype(np.int32)
+        toks = np.concatenate([np.zeros((B, 1), np.int32), kids], axis=1)
+        sid = torch.arange(c * B, (c + 1) * B, dtype=torch.int64, device=DEV)
+        res = sv.verify_tree(target, draft, torch.from_numpy(toks).to(DEV), parent,
+                             mode="multi_candidate", seed=8, seq_ids=sid, ws=ws)
+        first.append(res.out_tokens[:, 0].cpu().numpy())
+        depth.append(res.n_accepted.cpu().numpy())
+    first = np.concatenate(first)
+    depth = np.concatenate(depth)
+    bins = _bins(p0)
+    pv = _pvalue(first, p0, bins)
+    power = _pvalue(first, q0, bins)
+    print("p-value", pv, "power", power, "walks", len(first), "accepted a child", int((depth == 1).sum()),
+          flush=True)
+    assert depth.min() >= 0 and depth.max() <= 1
+    # both ways of emitting the first token occur often
+    assert len(first) // 5 < (depth == 1).sum() < len(first) - len(first) // 20
+    assert pv > THRESHOLD
+    assert power < 1e-6
