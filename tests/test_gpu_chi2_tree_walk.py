@@ -13,7 +13,11 @@ rejections; either way its law is p_root.  10^5 walks: 100 calls of 1000
 sequences, each with its own sequence id (so its own Philox uniforms) and
 its own four child tokens.  The expected law comes from scipy's softmax of
 the float32 rows the library reads; bins and threshold (10^-3) as in the
-window's pins at this size.  Power: the same statistic rejects q_root."""
+window's pins at this size.  Power: the same statistic rejects q_root.
+
+The second test pins the per-node stochastic tree the same way: with two
+children each tested against the root on its own, the first token's law is
+(1 - alpha) p + min(p, q), not p."""
 import numpy as np
 import pytest
 import torch
@@ -68,5 +72,44 @@ def test_gpu_walk_first_token_follows_p_root():
     assert depth.min() >= 0 and depth.max() <= 1
     # both ways of emitting the first token occur often
     assert len(first) // 5 < (depth == 1).sum() < len(first) - len(first) // 20
+    assert pv > THRESHOLD
+    assert power < 1e-6
+
+
+def test_gpu_per_node_tree_first_token_law():
+    """The per-node stochastic tree (SV_TREE_STOCHASTIC; "Accelerating LLM
+    Inference with Staged Speculative Decoding", abstract) at V = 32000 with
+    two children drawn i.i.d. from q_root: each child is tested against the
+    root's rows on its own, so the first token's law is (1 - alpha) p + min(p, q)
+    (alpha = sum min(p, q)), the closed form the oracle is pinned to by brute
+    force at V = 6.  10^5 trees; the same bins and threshold; power against
+    p_root itself."""
+    print("GPU per-node tree chi-square: 100 calls x 1000 trees, V=32000", flush=True)
+    T, D = _rows()
+    T, D = T[:3], D[:3]
+    p0 = sp_softmax(T[0].astype(np.float64))
+    q0 = sp_softmax(D[0].astype(np.float64))
+    law = (1.0 - np.minimum(p0, q0).sum()) * p0 + np.minimum(p0, q0)
+    cq = np.cumsum(q0)
+    parent = [-1, 0, 0]
+    N = len(parent)
+    target = torch.from_numpy(np.ascontiguousarray(T)).to(DEV)[None].expand(B, N, V).contiguous()
+    draft = torch.from_numpy(np.ascontiguousarray(D)).to(DEV)[None].expand(B, N, V).contiguous()
+    ws = sv.workspace(sv.SV_OP_TREE, B, N, V, torch.float32, DEV)
+    rng = np.random.default_rng(66)
+    first = []
+    for c in range(CALLS):
+        u = rng.random((B, 2))
+        kids = np.minimum(V - 1, np.searchsorted(cq, u * cq[-1], side="right")).astype(np.int32)
+        toks = np.concatenate([np.zeros((B, 1), np.int32), kids], axis=1)
+        sid = torch.arange(c * B, (c + 1) * B, dtype=torch.int64, device=DEV)
+        res = sv.verify_tree(target, draft, torch.from_numpy(toks).to(DEV), parent,
+                             mode="stochastic", seed=9, seq_ids=sid, ws=ws)
+        first.append(res.out_tokens[:, 0].cpu().numpy())
+    first = np.concatenate(first)
+    bins = _bins(law)
+    pv = _pvalue(first, law, bins)
+    power = _pvalue(first, p0, bins)
+    print("p-value", pv, "power", power, flush=True)
     assert pv > THRESHOLD
     assert power < 1e-6
