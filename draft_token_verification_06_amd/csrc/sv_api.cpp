@@ -477,14 +477,13 @@ int sv_verify_window_lmhead(const void *hidden_target, const void *unembed_targe
   float2 *part = reinterpret_cast<float2 *>(wsb + L.part_off);
   float2 *stats = reinterpret_cast<float2 *>(wsb + L.stats_off);
   float *gath = reinterpret_cast<float *>(wsb + L.gath_off);
-  int32_t *idx = reinterpret_cast<int32_t *>(wsb + L.idx_off);
   SampleJob *jobs = reinterpret_cast<SampleJob *>(wsb + L.jobs_off);
   const DrawScratch ds{reinterpret_cast<float *>(wsb + L.spart_off), L.cmax,
                        reinterpret_cast<int32_t *>(wsb + L.arrive_off)};
   float *rows_t = reinterpret_cast<float *>(wsb + L.rows_t_off);
   float *rows_d = reinterpret_cast<float *>(wsb + L.rows_d_off);
 
-  // pass 1: every target and draft row, statistics and the draft-token logits
+  // every target and draft row: float32 logits, statistics and the draft-token logits
   LmGemmArgs G{};
   G.A = static_cast<const uint16_t *>(hidden_target);
   G.lda = Ht;
@@ -497,6 +496,7 @@ int sv_verify_window_lmhead(const void *hidden_target, const void *unembed_targe
   G.tokens = draft_tokens;
   G.gamma = gamma;
   G.rows_per_seq = gamma + 1;
+  G.out = rows_t;
   LmGemmArgs Gd = G;
   Gd.A = static_cast<const uint16_t *>(hidden_draft);
   Gd.lda = Hd;
@@ -506,7 +506,8 @@ int sv_verify_window_lmhead(const void *hidden_target, const void *unembed_targe
   Gd.part = part + Mt * L.NT;
   Gd.gath = gath + Mt;
   Gd.rows_per_seq = gamma;
-  launch_lm_gemm(LM_STATS, G, Gd, stream);
+  Gd.out = rows_d;
+  launch_lm_gemm(G, Gd, stream);
   launch_lm_combine(part, L.NT, static_cast<int>(Mt + Md), stats, stream);
 
   LmDecideArgs D{};
@@ -529,21 +530,8 @@ int sv_verify_window_lmhead(const void *hidden_target, const void *unembed_targe
   D.jobs = jobs;
   D.rows_t = rows_t;
   D.rows_d = rows_d;
-  D.idx_t = idx;
-  D.idx_d = idx + B;
   D.arrive = ds.arrive;
   launch_lm_decide(D, B, stream);
-
-  // pass 2: target row n and draft row n of every sequence, stored in float32
-  LmGemmArgs S = G;
-  S.a_rows = idx;
-  S.M = B;
-  S.out = rows_t;
-  LmGemmArgs Sd = Gd;
-  Sd.a_rows = idx + B;
-  Sd.M = B;
-  Sd.out = rows_d;
-  launch_lm_gemm(LM_STORE, S, Sd, stream);
 
   launch_tree_finish(SV_DT_F32, jobs, B, V, ds, stream);
   return launch_status();

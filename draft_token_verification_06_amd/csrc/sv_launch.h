@@ -63,21 +63,19 @@ struct RollbackArgs {
   int32_t len_offset;
 };
 
-// LM-head fused window.  GEMM rows g < M: hidden row (a_rows ? a_rows[g] : g)
-// of A (row stride lda elements) against every row of W ([V][K], bf16).
-enum : int { LM_STATS = 0, LM_STORE = 1 };
+// LM-head fused window.  GEMM rows g < M: hidden row g of A (row stride lda
+// elements) against every row of W ([V][K], bf16).
 struct LmGemmArgs {
   const uint16_t *A;
   int64_t lda;
-  const int32_t *a_rows;
   const uint16_t *W;
   int32_t M, V, K;
   int32_t RB, NT;             // row blocks, column tiles (set by the launcher)
-  float2 *part;               // STATS: [M][NT] (max, sum-exp) per row and column tile
-  float *gath;                // STATS: [M] logit at the row's draft token
-  const int32_t *tokens;      // STATS: [B][gamma]
+  float2 *part;               // [M][NT] (max, sum-exp) per row and column tile
+  float *gath;                // [M] logit at the row's draft token
+  const int32_t *tokens;      // [B][gamma]
   int32_t gamma, rows_per_seq;
-  float *out;                 // STORE: [M][V] float32 logits
+  float *out;                 // [M][V] float32 logits
 };
 
 struct LmDecideArgs {
@@ -92,13 +90,12 @@ struct LmDecideArgs {
   int32_t *n_accepted, *out_tokens;
   float *p_draft, *q_draft;
   SampleJob *jobs;
-  const float *rows_t, *rows_d;  // where the second pass stores target / draft row n
-  int32_t *idx_t, *idx_d;        // hidden rows of that pass
+  const float *rows_t, *rows_d;  // the GEMM's float32 logits, [B][gamma+1][V] / [B][gamma][V]
   int32_t *arrive;               // arrival counters of the draw, zeroed here
 };
 
 // Launches the GEMMs of two problems (target rows, draft rows) as one grid.
-void launch_lm_gemm(int mode, LmGemmArgs A0, LmGemmArgs A1, hipStream_t st);
+void launch_lm_gemm(LmGemmArgs A0, LmGemmArgs A1, hipStream_t st);
 int lm_gemm_blocks(int M, int V);
 void launch_lm_combine(const float2 *part, int NT, int M, float2 *stats, hipStream_t st);
 void launch_lm_decide(const LmDecideArgs &A, int B, hipStream_t st);

@@ -1,8 +1,9 @@
 // LM head fused with verification (gfx950): logits = hidden x unembedding^T
-// on the matrix cores, consumed tile by tile by the row statistics, so the
-// logits never travel through HBM.  Only the rows a draw needs (target row n
-// and draft row n of each sequence) are recomputed by the same kernel and
-// stored, in float32, for the sampling pass.
+// on the matrix cores, consumed tile by tile by the row statistics, so no
+// pass reads the logits back to reduce them.  The same epilogue writes the
+// float32 logits out with nontemporal stores (the writes overlap the other
+// blocks' matrix work); the sampling pass then reads only the rows a draw
+// needs, target row n and draft row n of each sequence.
 //
 // GEMM: C[M x V] = A[M x K] * W[V x K]^T, bf16 inputs, float32 accumulation in
 // v_mfma_f32_32x32x16_bf16.  Block tile 256 x 256, K step 64, 8 waves of 64 x
@@ -69,7 +70,6 @@ __device__ __forceinline__ float lm_swap16(float x) {
 }
 
 // One 256 x 256 output tile of problem P; L is the block's index within P.
-template <int kMode>
 __device__ __forceinline__ void lm_gemm_tile(const LmGemmArgs &P, int L) {
   __shared__ uint4 lds_raw[2 * kStageElems * sizeof(uint16_t) / sizeof(uint4)];
   uint16_t *lds = reinterpret_cast<uint16_t *>(lds_raw);
@@ -92,7 +92,7 @@ __device__ __forceinline__ void lm_gemm_tile(const LmGemmArgs &P, int L) {
     const int q = tid + kGemmThreads * j;
     const int r = q / kChunksK, ch = q % kChunksK;
     const int gr = row0 + r;
-    const int64_t arow = gr < P.M ? (P.a_rows ? P.a_rows[gr] : gr) : 0;
+    const int64_t arow = gr < P.M ? gr : 0;
     asrc[j] = reinterpret_cast<const uint4 *>(P.A + arow * P.lda + ch * 8);
     aoff[j] = r * kLdsRow + ch * 8;
   }
@@ -104,7 +104,7 @@ __device__ __forceinline__ void lm_gemm_tile(const LmGemmArgs &P, int L) {
     wsrc[j] = reinterpret_cast<const uint4 *>(P.W + static_cast<int64_t>(gc < P.V ? gc : 0) * P.K + ch * 8);
     woff[j] = kBM * kLdsRow + r * kLdsRow + ch * 8;
   }
-  if (kMode == LM_STATS && tid < kBM) {
+  if (tid < kBM) {
     const int g = row0 + tid;
     int x = -1;
     if (g < P.M) {
@@ -215,23 +215,6 @@ __device__ __forceinline__ void lm_gemm_tile(const LmGemmArgs &P, int L) {
 #undef SV_LM_STORE1
 #undef SV_LM_LOAD1
 
-  if (kMode == LM_STORE) {
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int g = row0 + wm * kWaveM + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (g >= P.M) continue;
-        float *orow = P.out + static_cast<int64_t>(g) * P.V;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int col = col0 + wn * 128 + nt * 32 + c32;
-          if (col < P.V) orow[col] = acc[mt][nt][r];
-        }
-      }
-    return;
-  }
-
   // Row statistics of this wave's 128 columns: max, then sum of exp(x - max)
   // (the same 2^(x log2e - m log2e) form as the streaming row pass), across
   // the 32 lanes of each half-wave: within each row of 16 lanes by DPP
@@ -240,7 +223,8 @@ __device__ __forceinline__ void lm_gemm_tile(const LmGemmArgs &P, int L) {
   // half's j-th row (and row j + 32 with four row tiles), so the loop has no
   // branches and one LDS store per lane ends it.  The lane holding a row's
   // draft-token column leaves that logit in s_gath (other lanes write a
-  // scratch slot of their own).
+  // scratch slot of their own).  Each lane also writes its logits of rows
+  // below M: 32 consecutive columns per half-wave and store.
   const bool full = col0 + kBN <= P.V;
   const int cbase = col0 + wn * 128 + c32;
   constexpr int kKeep = kMT / 2;
@@ -260,6 +244,12 @@ __device__ __forceinline__ void lm_gemm_tile(const LmGemmArgs &P, int L) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
         v[nt] = (!decltype(masked)::value || cbase + nt * 32 < P.V) ? acc[mt][nt][r] : kNegInf;
+      if (row0 + rl < P.M) {
+        float *orow = P.out + static_cast<int64_t>(row0 + rl) * P.V + cbase;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          if (!decltype(masked)::value || cbase + nt * 32 < P.V) __builtin_nontemporal_store(acc[mt][nt][r], orow + nt * 32);
+      }
       float m = lm_max(lm_max(v[0], v[1]), lm_max(v[2], v[3]));
       m = lm_max(m, lm_dpp<0xB1>(m));
       m = lm_max(m, lm_dpp<0x4E>(m));
@@ -306,18 +296,18 @@ __device__ __forceinline__ void lm_gemm_tile(const LmGemmArgs &P, int L) {
   }
 }
 
-// Two GEMM problems in one launch (target and draft rows): blocks [0, blocks0)
-// take P0, the rest P1.  One launch fills the tail of the first problem's
-// last round of blocks with the second's.  blocks0 is a multiple of 8, so
-// both problems keep the XCD-aware tile map.
-template <int kMode>
+// Two GEMM problems in one launch (target and draft rows, the same column
+// tiles): blocks [0, blocks0) take P0, the rest P1, so the last rounds run
+// the tiles with fewer K steps when the draft's hidden width is smaller.
+// blocks0 is a multiple of 8, so both problems keep the XCD-aware tile map.
 __global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(kGemmThreads / 256)))
-k_lm_gemm(LmGemmArgs P0, LmGemmArgs P1, int blocks0) {
+k_lm_gemm(LmGemmArgs P0, LmGemmArgs P1) {
+  const int blocks0 = 8 * ((P0.NT + 7) / 8) * P0.RB;
   const int L = blockIdx.x;
   if (L < blocks0)
-    lm_gemm_tile<kMode>(P0, L);
+    lm_gemm_tile(P0, L);
   else
-    lm_gemm_tile<kMode>(P1, L - blocks0);
+    lm_gemm_tile(P1, L - blocks0);
 }
 
 // Per row, the column-tile partials in a fixed order: lane-strided, then the
@@ -345,8 +335,8 @@ __device__ __forceinline__ float lm_offset(float2 st) { return st.x * kLog2e + l
 // Window decision from the fused statistics (one wave per sequence, lane i =
 // position i): p_i(x_i), q_i(x_i) from the row statistics and the logits at the
 // draft tokens; accept iff u q < p; the first rejection ends the window.
-// Writes the window outputs, the sampling job (rows in the workspace, filled
-// by the second GEMM pass) and the hidden-state rows that pass needs.
+// Writes the window outputs and the sampling job, which points at target row
+// n and draft row n of the logits the GEMM wrote.
 __global__ void __launch_bounds__(kWave) k_lm_decide(LmDecideArgs A) {
   const int b = blockIdx.x;
   const int i = threadIdx.x;
@@ -366,8 +356,6 @@ __global__ void __launch_bounds__(kWave) k_lm_decide(LmDecideArgs A) {
     if (i == 0) {
       A.n_accepted[b] = -1;
       A.jobs[b].mode = JOB_NONE;
-      A.idx_t[b] = b * (g + 1);
-      A.idx_d[b] = b * g;
     }
     return;
   }
@@ -398,11 +386,11 @@ __global__ void __launch_bounds__(kWave) k_lm_decide(LmDecideArgs A) {
       v = uniform24(w2.c1);
     }
     SampleJob jb{};
-    jb.t_row = A.rows_t + static_cast<int64_t>(b) * A.V;
+    jb.t_row = A.rows_t + (rt + n) * A.V;
     jb.ct = lm_offset(A.stats_t[rt + n]);
     if (n < len) {
       jb.mode = JOB_RESIDUAL;
-      jb.d_row = A.rows_d + static_cast<int64_t>(b) * A.V;
+      jb.d_row = A.rows_d + (rd + n) * A.V;
       jb.cd = lm_offset(A.stats_d[rd + n]);
       jb.cq = 1.0f;
     } else {
@@ -413,8 +401,6 @@ __global__ void __launch_bounds__(kWave) k_lm_decide(LmDecideArgs A) {
     jb.out_slot = out + n;
     A.jobs[b] = jb;
     A.n_accepted[b] = n;
-    A.idx_t[b] = static_cast<int32_t>(rt + n);
-    A.idx_d[b] = static_cast<int32_t>(rd + min(n, g - 1));
   }
 }
 
@@ -423,17 +409,13 @@ int lm_gemm_blocks(int M, int V) {
   return 8 * ((NT + 7) / 8) * RB;
 }
 
-void launch_lm_gemm(int mode, LmGemmArgs A0, LmGemmArgs A1, hipStream_t st) {
+void launch_lm_gemm(LmGemmArgs A0, LmGemmArgs A1, hipStream_t st) {
   A0.RB = (A0.M + kBM - 1) / kBM;
   A0.NT = (A0.V + kBN - 1) / kBN;
   A1.RB = (A1.M + kBM - 1) / kBM;
   A1.NT = (A1.V + kBN - 1) / kBN;
-  const int blocks0 = lm_gemm_blocks(A0.M, A0.V);
-  const int blocks = blocks0 + lm_gemm_blocks(A1.M, A1.V);
-  if (mode == LM_STATS)
-    hipLaunchKernelGGL(k_lm_gemm<LM_STATS>, dim3(blocks), dim3(kGemmThreads), 0, st, A0, A1, blocks0);
-  else
-    hipLaunchKernelGGL(k_lm_gemm<LM_STORE>, dim3(blocks), dim3(kGemmThreads), 0, st, A0, A1, blocks0);
+  const int blocks = lm_gemm_blocks(A0.M, A0.V) + lm_gemm_blocks(A1.M, A1.V);
+  hipLaunchKernelGGL(k_lm_gemm, dim3(blocks), dim3(kGemmThreads), 0, st, A0, A1);
 }
 
 void launch_lm_combine(const float2 *part, int NT, int M, float2 *stats, hipStream_t st) {

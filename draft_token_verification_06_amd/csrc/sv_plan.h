@@ -123,7 +123,7 @@ inline Layout make_layout(int op, int64_t B, int32_t n, int32_t V) {
 struct LmLayout {
   int NT;  // column tiles
   int cmax;
-  size_t part_off, stats_off, gath_off, idx_off, jobs_off, spart_off, arrive_off, rows_t_off, rows_d_off, total;
+  size_t part_off, stats_off, gath_off, jobs_off, spart_off, arrive_off, rows_t_off, rows_d_off, total;
 };
 
 inline LmLayout make_lm_layout(int64_t B, int32_t gamma, int32_t V) {
@@ -138,8 +138,6 @@ inline LmLayout make_lm_layout(int64_t B, int32_t gamma, int32_t V) {
   off = align256(off + sizeof(float) * 2 * static_cast<size_t>(M));
   L.gath_off = off;
   off = align256(off + sizeof(float) * static_cast<size_t>(M));
-  L.idx_off = off;
-  off = align256(off + sizeof(int32_t) * 2 * static_cast<size_t>(B));
   L.jobs_off = off;
   off = align256(off + sizeof(SampleJob) * static_cast<size_t>(B));
   L.spart_off = off;
@@ -147,9 +145,9 @@ inline LmLayout make_lm_layout(int64_t B, int32_t gamma, int32_t V) {
   L.arrive_off = off;
   off = align256(off + sizeof(int32_t) * static_cast<size_t>(B));
   L.rows_t_off = off;
-  off = align256(off + sizeof(float) * static_cast<size_t>(B) * V);
+  off = align256(off + sizeof(float) * static_cast<size_t>(Mt) * V);
   L.rows_d_off = off;
-  off = align256(off + sizeof(float) * static_cast<size_t>(B) * V);
+  off = align256(off + sizeof(float) * static_cast<size_t>(Md) * V);
   L.total = off;
   return L;
 }

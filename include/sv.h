@@ -279,18 +279,20 @@ int sv_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t str
  *   target row i of sequence b = hidden_target[b][i] . unembed_target[k] for k < V,
  *   draft  row i of sequence b = hidden_draft[b][i]  . unembed_draft[k],
  * dot products of bf16 values accumulated in float32 on the matrix cores.
- * The logits never go to memory: each GEMM tile feeds the row statistics and
- * the logits at the draft tokens directly.  The rows a draw needs (target row
- * n and draft row n of each sequence) are recomputed by the same tiles and
- * stored in float32 in the workspace.  This is an extension beyond the pages,
- * which only say that draft and target models produce the distributions.
+ * Each GEMM tile feeds the row statistics and the logits at the draft tokens
+ * directly, so no pass reads the logits back to reduce them; the same tiles
+ * write the float32 logits to the workspace, and the draw reads only target
+ * row n and draft row n of each sequence there.  This is an extension beyond
+ * the pages, which only say that draft and target models produce the
+ * distributions.
  *   hidden_target [B][gamma+1][Ht] bf16, unembed_target [V][Ht] bf16,
  *   hidden_draft  [B][gamma][Hd]   bf16, unembed_draft  [V][Hd] bf16; dense,
  *   16-byte aligned; Ht, Hd multiples of SV_LMHEAD_K_STEP, at most
  *   SV_LMHEAD_MAX_HIDDEN.
  *   Other arguments and outputs as sv_verify_window; workspace of
- *   sv_workspace_size(SV_OP_LMHEAD, B, gamma, V, SV_DT_BF16) bytes (it holds two
- *   float32 vocabulary rows per sequence).
+ *   sv_workspace_size(SV_OP_LMHEAD, B, gamma, V, SV_DT_BF16) bytes (it holds
+ *   the 2 gamma + 1 float32 logit rows of every sequence: 2.25 GB at B = 256,
+ *   gamma = 8, V = 128256).
  * Errors: as sv_verify_window; SV_EINVAL for hidden sizes outside the rules. */
 int sv_verify_window_lmhead(const void *hidden_target, const void *unembed_target, int32_t Ht,
                             const void *hidden_draft, const void *unembed_draft, int32_t Hd,
