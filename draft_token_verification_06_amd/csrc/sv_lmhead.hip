@@ -1,9 +1,10 @@
 // LM head fused with verification (gfx950): logits = hidden x unembedding^T
 // on the matrix cores, consumed tile by tile by the row statistics, so no
 // pass reads the logits back to reduce them.  The same epilogue writes the
-// float32 logits out with nontemporal stores (the writes overlap the other
-// blocks' matrix work); the sampling pass then reads only the rows a draw
-// needs, target row n and draft row n of each sequence.
+// float32 logits out with nontemporal stores, and the sampling pass reads
+// only the rows a draw needs, target row n and draft row n of each sequence.
+// The writes lengthen the launch in proportion to their bytes, by less than
+// a second GEMM over the drawn rows would take.
 //
 // GEMM: C[M x V] = A[M x K] * W[V x K]^T, bf16 inputs, float32 accumulation in
 // v_mfma_f32_32x32x16_bf16.  Block tile 256 x 256, K step 64, 8 waves of 64 x
