@@ -299,11 +299,12 @@ def lmhead_logit_tol(logits, K):
     return 4.0 * 2.0 ** -24 * np.sqrt(K / 16.0) * float(np.max(np.abs(logits)))
 
 
-def check_lmhead(data, res, *, seed, tag=0, window_len=None, rows=None):
+def check_lmhead(data, res, *, seed, tag=0, window_len=None, seq_ids=None, base_pos=None, rows=None):
     """Compares sv_verify_window_lmhead with oracle.verify_window_lmhead on the
-    sequences `rows`.  Tolerances: the window's (1e-5) plus twice the logit
-    allowance of lmhead_logit_tol (token logit and log-normaliser both carry
-    it).  Returns (n_checked, n_margin_cases)."""
+    sequences `rows`, with the uniforms keyed by (seed, tag; seq_ids[b] or b,
+    base_pos[b] or 0) as in check_window.  Tolerances: the window's (1e-5) plus
+    twice the logit allowance of lmhead_logit_tol (token logit and
+    log-normaliser both carry it).  Returns (n_checked, n_margin_cases)."""
     gamma, B = data["gamma"], data["B"]
     rows = range(B) if rows is None else rows
     Wt = host_rows(data["w_target"], "bf16")
@@ -315,6 +316,8 @@ def check_lmhead(data, res, *, seed, tag=0, window_len=None, rows=None):
     Q_gpu = res.q_draft.cpu().numpy() if res.q_draft is not None else None
     toks = data["tokens"].cpu().numpy()
     wl = window_len.cpu().numpy() if window_len is not None else None
+    sid = seq_ids.cpu().numpy() if seq_ids is not None else None
+    bp = base_pos.cpu().numpy() if base_pos is not None else None
     margins = 0
     for b in rows:
         T = oracle.lmhead_logits(host_rows(data["h_target"][b], "bf16"), Wt)
@@ -322,7 +325,9 @@ def check_lmhead(data, res, *, seed, tag=0, window_len=None, rows=None):
         tp = PROB_RTOL + 2 * lmhead_logit_tol(T, Kt)
         tq = PROB_RTOL + 2 * lmhead_logit_tol(D, Kd)
         length = int(wl[b]) if wl is not None else gamma
-        u, v = oracle.window_uniforms(seed, tag, b, 0, gamma)
+        s = int(sid[b]) if sid is not None else b
+        base = int(bp[b]) if bp is not None else 0
+        u, v = oracle.window_uniforms(seed, tag, s, base, gamma)
         o = oracle.verify_window(T, D, toks[b], length, u, v)
         if P_gpu is not None:
             for i in range(min(o["n"] + 1, length)):

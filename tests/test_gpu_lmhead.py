@@ -2,8 +2,9 @@
 with the window) against oracle.verify_window_lmhead (float64 logits from the
 same bf16 hidden states and unembeddings): p(x), q(x) within 1e-5 relative,
 n and tokens identical except margin cases (at most one per test); ragged
-row and column tiles, partial windows, invalid tokens, small batches (split
-draw) and the 8B/1B-shaped workload on sampled sequences."""
+row and column tiles, partial windows, invalid tokens, caller-chosen uniform
+keys, small batches (split draw) and the 8B/1B-shaped workload on sampled
+sequences."""
 import numpy as np
 import pytest
 import torch
@@ -48,6 +49,27 @@ def test_lmhead_partial_windows_and_invalid_tokens():
     rows = [b for b in range(B) if b != 8]
     n, m = check_lmhead(d, res, seed=3, window_len=wl, rows=rows)
     assert m <= 1
+
+
+@pytest.mark.parametrize("B", [5, 300])
+def test_lmhead_caller_keys(B):
+    """Uniforms keyed by the caller: random sequence ids and base positions
+    and a nonzero tag, drawn through both draw launches (float32 rows of
+    V = 9000 are three 16 KB chunks: at B = 5 each sequence's draw is split over
+    three workgroups and the last to finish draws; at B = 300 one workgroup
+    draws).  Every sequence is checked against the oracle with the same keys."""
+    print("lmhead caller keys", B, flush=True)
+    gamma, V = 4, 9000
+    d = synth.lmhead_batch(B, gamma, V, 128, 64, seed=500 + B, device=DEV)
+    rng = np.random.default_rng(77 + B)
+    sid = torch.from_numpy(rng.integers(0, 2 ** 40, B).astype(np.int64)).to(DEV)
+    bp = torch.from_numpy(rng.integers(0, 10 ** 6, B).astype(np.int64)).to(DEV)
+    res = _run(d, seed=9, tag=3, seq_ids=sid, base_pos=bp)
+    n, m = check_lmhead(d, res, seed=9, tag=3, seq_ids=sid, base_pos=bp)
+    assert n == B and m <= 1
+    # the keys matter: the default keys give other decisions somewhere
+    plain = _run(d, seed=9)
+    assert not torch.equal(plain.out_tokens, res.out_tokens)
 
 
 def test_lmhead_8b_1b_shape_sampled():
