@@ -50,6 +50,30 @@ __device__ __forceinline__ MaxSum row_maxsum(const float2 *p, int S) {
   return r;
 }
 
+// The results of two rows (a target row and its draft row) at once, each
+// combined in segment order as row_maxsum does: both rows' loads go out
+// before either is combined, so the pair costs one row's round trips.  pa and
+// pb must point at S readable results whatever the flags: the loads are not
+// predicated per lane (a lane-predicated load waits for its data on its own),
+// and a row whose flag is false keeps the value it came with.
+__device__ __forceinline__ void row_maxsum_pair(const float2 *pa, bool la, const float2 *pb, bool lb, int S,
+                                                MaxSum &ra, MaxSum &rb) {
+  for (int k0 = 0; k0 < S; k0 += kSegBatch) {
+    float2 qa[kSegBatch], qb[kSegBatch];
+#pragma unroll
+    for (int j = 0; j < kSegBatch; ++j)
+      if (k0 + j < S) {
+        qa[j] = pa[k0 + j];
+        qb[j] = pb[k0 + j];
+      }
+#pragma unroll
+    for (int j = 0; j < kSegBatch; ++j) {
+      if (la && k0 + j < S) ra = k0 + j == 0 ? MaxSum{qa[j].x, qa[j].y} : combine(ra, MaxSum{qa[j].x, qa[j].y});
+      if (lb && k0 + j < S) rb = k0 + j == 0 ? MaxSum{qb[j].x, qb[j].y} : combine(rb, MaxSum{qb[j].x, qb[j].y});
+    }
+  }
+}
+
 __device__ __forceinline__ MaxIdx row_argmax(const float2 *p, int S) {
   MaxIdx r{kNegInf, 0};
   for (int k0 = 0; k0 < S; k0 += kSegBatch) {
@@ -90,6 +114,17 @@ __device__ void window_decide(const WindowArgs &A, int b, int i, bool write, Sam
   int32_t *out = A.out_tokens + static_cast<int64_t>(b) * (A.gamma + 1);
   const int len = A.window_len ? A.window_len[b] : A.gamma;
   const int xi = i < A.gamma ? A.tokens[static_cast<int64_t>(b) * A.gamma + i] : 0;
+  // The ids and the row results of target row i (i <= gamma) and draft row i
+  // (i < gamma) are loaded before the window is checked, whatever its length
+  // (rows past it, and those of a sequence found invalid, hold stale values
+  // that are not used), so they travel with the token loads; only the two
+  // logit gathers wait for the token.
+  const float2 *prow = A.part + static_cast<int64_t>(b) * R * A.S;
+  MaxSum st{0.0f, 1.0f}, sd{0.0f, 1.0f};
+  row_maxsum_pair(prow + min(i, A.gamma) * A.S, i <= A.gamma, prow + (A.gamma + 1 + min(i, A.gamma - 1)) * A.S,
+                  i < A.gamma, A.S, st, sd);
+  const uint64_t seq = A.seq_ids ? A.seq_ids[b] : static_cast<uint64_t>(b);
+  const int64_t base = A.base_pos ? A.base_pos[b] : 0;
   const bool bad_len = len < 0 || len > A.gamma;
   const bool bad_tok = !bad_len && i < len && (xi < 0 || xi >= A.V);
   if (__any(bad_len || bad_tok)) {
@@ -105,20 +140,9 @@ __device__ void window_decide(const WindowArgs &A, int b, int i, bool write, Sam
     return;
   }
   const int x = i < len ? xi : 0;
-  const float2 *prow = A.part + static_cast<int64_t>(b) * R * A.S;
   const char *trow0 = A.t + b * A.t_stride_bytes;
   const char *drow0 = A.d + b * A.d_stride_bytes;
   const int64_t row_bytes = static_cast<int64_t>(A.V) * E::kBytes;
-  const uint64_t seq = A.seq_ids ? A.seq_ids[b] : static_cast<uint64_t>(b);
-  const int64_t base = A.base_pos ? A.base_pos[b] : 0;
-
-  // Row results of target row i (i <= gamma) and draft row i (i < gamma) are
-  // loaded whatever the window length (rows past it hold stale values and are
-  // not used), so they travel with the token loads; only the two logit
-  // gathers wait for the token.
-  MaxSum st{0.0f, 1.0f}, sd{0.0f, 1.0f};
-  if (i <= A.gamma) st = row_maxsum(prow + i * A.S, A.S);
-  if (i < A.gamma) sd = row_maxsum(prow + (A.gamma + 1 + i) * A.S, A.S);
   const U64x4 w = philox4x64_10({seq, static_cast<uint64_t>(base + 1 + i), 0, 0}, A.seed, A.tag);
   const float vi = uniform24(w.c1);
   float P = 0.0f, Q = 0.0f;
@@ -198,8 +222,8 @@ __device__ __forceinline__ void stage_decide(const WindowArgs &A, int b, int i, 
   const int64_t base = A.base_pos ? A.base_pos[b] : 0;
   const float2 *prow = A.part + static_cast<int64_t>(b) * R * A.S;
   MaxSum st{0.0f, 1.0f}, sd{0.0f, 1.0f};
-  if (p < hi) st = row_maxsum(prow + p * A.S, A.S);
-  if (p < hi && p < A.gamma) sd = row_maxsum(prow + (A.gamma + 1 + p) * A.S, A.S);
+  row_maxsum_pair(prow + min(p, hi - 1) * A.S, p < hi, prow + (A.gamma + 1 + min(p, A.gamma - 1)) * A.S,
+                  p < hi && p < A.gamma, A.S, st, sd);
   if (stat != kSeqVerifying) return;
   if (lo == 0) {
     const bool bad_len = len < 0 || len > A.gamma;
@@ -346,14 +370,12 @@ __device__ void tree_decide(const TreeArgs &A, int b, int v, bool write, SampleJ
   const int64_t base = A.base_pos ? A.base_pos[b] : 0;
   int am = -1;
   MaxSum st{0.0f, 1.0f}, sd{0.0f, 1.0f};
-  if (v >= 1 && v < N) {
-    const int w = A.meta.parent[v];
-    if (A.mode == 0) {
-      am = row_argmax(prow + w * A.S, A.S).i;
-    } else {
-      st = row_maxsum(prow + w * A.S, A.S);
-      sd = row_maxsum(prow + (N + w) * A.S, A.S);
-    }
+  const bool node = v >= 1 && v < N;
+  const int pw = node ? A.meta.parent[v] : 0;  // row 0 stands in for threads without a node
+  if (A.mode == 0) {
+    if (node) am = row_argmax(prow + pw * A.S, A.S).i;
+  } else {
+    row_maxsum_pair(prow + pw * A.S, node, prow + (N + pw) * A.S, node, A.S, st, sd);
   }
   const bool bad = v >= 1 && v < N && (tok < 0 || tok >= A.V);
   if (__syncthreads_or(bad)) {
@@ -969,15 +991,17 @@ __global__ void __launch_bounds__(kFinThreads) k_tree_walk(TreeArgs A) {
     const int first = A.meta.first_child[v];
     const int depth = A.meta.depth[v];
     const int rank = A.meta.rank[v];
-    s_ct[v] = norm_offset(row_maxsum(prow + v * A.S, A.S));
-    s_cd[v] = first >= 0 ? norm_offset(row_maxsum(prow + (N + v) * A.S, A.S)) : 0.0f;
+    // rows v and the parent's rows w: all four rows' results in one go
+    const int w = v >= 1 ? A.meta.parent[v] : 0;
+    MaxSum mt{0.0f, 1.0f}, md{0.0f, 1.0f}, st{0.0f, 1.0f}, sd{0.0f, 1.0f};
+    row_maxsum_pair(prow + v * A.S, true, prow + (N + v) * A.S, first >= 0, A.S, mt, md);
+    row_maxsum_pair(prow + w * A.S, v >= 1, prow + (N + w) * A.S, v >= 1, A.S, st, sd);
+    s_ct[v] = norm_offset(mt);
+    s_cd[v] = first >= 0 ? norm_offset(md) : 0.0f;
     s_v[v] = uniform24(
         philox4x64_10({seq, static_cast<uint64_t>(base + depth + 1), static_cast<uint64_t>(rank), 0}, A.seed, A.tag)
             .c1);
     if (v >= 1) {
-      const int w = A.meta.parent[v];
-      const MaxSum st = row_maxsum(prow + w * A.S, A.S);
-      const MaxSum sd = row_maxsum(prow + (N + w) * A.S, A.S);
       s_P[v] = prob_at(E::one(t0 + w * row_bytes, tok), st);
       s_Q[v] = prob_at(E::one(d0 + w * row_bytes, tok), sd);
       s_u[v] = uniform24(

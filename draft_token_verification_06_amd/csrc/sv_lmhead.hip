@@ -345,8 +345,22 @@ __global__ void __launch_bounds__(kWave) k_lm_decide(LmDecideArgs A) {
   const int g = A.gamma;
   int32_t *out = A.out_tokens + static_cast<int64_t>(b) * (g + 1);
   const int len = A.window_len ? A.window_len[b] : g;
-  const bool bad_len = len < 0 || len > g;
   const int x = i < g ? A.tokens[static_cast<int64_t>(b) * g + i] : 0;
+  // the ids and the statistics and token logits of rows i go out with the
+  // token loads, before the window is checked (values of an invalid
+  // sequence, or past its window, are not used)
+  const uint64_t seq = A.seq_ids ? A.seq_ids[b] : static_cast<uint64_t>(b);
+  const int64_t base = A.base_pos ? A.base_pos[b] : 0;
+  const int64_t rt = static_cast<int64_t>(b) * (g + 1), rd = static_cast<int64_t>(b) * g;
+  float2 sti{0.0f, 1.0f}, sdi{0.0f, 1.0f};
+  float gti = 0.0f, gdi = 0.0f;
+  if (i < g) {
+    sti = A.stats_t[rt + i];
+    gti = A.gath_t[rt + i];
+    sdi = A.stats_d[rd + i];
+    gdi = A.gath_d[rd + i];
+  }
+  const bool bad_len = len < 0 || len > g;
   const bool bad_tok = !bad_len && i < len && (x < 0 || x >= A.V);
   if (__any(bad_len || bad_tok)) {
     for (int k = i; k <= g; k += kWave) out[k] = -1;
@@ -360,15 +374,12 @@ __global__ void __launch_bounds__(kWave) k_lm_decide(LmDecideArgs A) {
     }
     return;
   }
-  const uint64_t seq = A.seq_ids ? A.seq_ids[b] : static_cast<uint64_t>(b);
-  const int64_t base = A.base_pos ? A.base_pos[b] : 0;
-  const int64_t rt = static_cast<int64_t>(b) * (g + 1), rd = static_cast<int64_t>(b) * g;
   const U64x4 w = philox4x64_10({seq, static_cast<uint64_t>(base + 1 + i), 0, 0}, A.seed, A.tag);
   float P = 0.0f, Q = 0.0f;
   bool acc = false;
   if (i < len) {
-    P = lm_prob(A.gath_t[rt + i], A.stats_t[rt + i]);
-    Q = lm_prob(A.gath_d[rd + i], A.stats_d[rd + i]);
+    P = lm_prob(gti, sti);
+    Q = lm_prob(gdi, sdi);
     acc = uniform24(w.c0) * Q < P;
   }
   const uint64_t inv = ~static_cast<uint64_t>(__ballot(acc));
