@@ -114,11 +114,11 @@ __device__ void window_decide(const WindowArgs &A, int b, int i, bool write, Sam
   int32_t *out = A.out_tokens + static_cast<int64_t>(b) * (A.gamma + 1);
   const int len = A.window_len ? A.window_len[b] : A.gamma;
   const int xi = i < A.gamma ? A.tokens[static_cast<int64_t>(b) * A.gamma + i] : 0;
-  // The ids and the row results of target row i (i <= gamma) and draft row i
-  // (i < gamma) are loaded before the window is checked, whatever its length
-  // (rows past it, and those of a sequence found invalid, hold stale values
-  // that are not used), so they travel with the token loads; only the two
-  // logit gathers wait for the token.
+  // The row results of target row i (i <= gamma) and draft row i (i < gamma)
+  // are loaded before the window is checked, whatever its length (rows past
+  // it, and those of a sequence found invalid, hold stale values that are not
+  // used), so they travel with the token loads; only the two logit gathers
+  // wait for the token.
   const float2 *prow = A.part + static_cast<int64_t>(b) * R * A.S;
   MaxSum st{0.0f, 1.0f}, sd{0.0f, 1.0f};
   row_maxsum_pair(prow + min(i, A.gamma) * A.S, i <= A.gamma, prow + (A.gamma + 1 + min(i, A.gamma - 1)) * A.S,
@@ -373,7 +373,8 @@ __device__ void tree_decide(const TreeArgs &A, int b, int v, bool write, SampleJ
   const bool node = v >= 1 && v < N;
   const int pw = node ? A.meta.parent[v] : 0;  // row 0 stands in for threads without a node
   if (A.mode == 0) {
-    if (node) am = row_argmax(prow + pw * A.S, A.S).i;
+    const int a = row_argmax(prow + pw * A.S, A.S).i;  // unpredicated load (row 0 stands in)
+    am = node ? a : -1;
   } else {
     row_maxsum_pair(prow + pw * A.S, node, prow + (N + pw) * A.S, node, A.S, st, sd);
   }
@@ -991,7 +992,7 @@ __global__ void __launch_bounds__(kFinThreads) k_tree_walk(TreeArgs A) {
     const int first = A.meta.first_child[v];
     const int depth = A.meta.depth[v];
     const int rank = A.meta.rank[v];
-    // rows v and the parent's rows w: all four rows' results in one go
+    // results of rows v and of the parent's rows w, each pair as one batch
     const int w = v >= 1 ? A.meta.parent[v] : 0;
     MaxSum mt{0.0f, 1.0f}, md{0.0f, 1.0f}, st{0.0f, 1.0f}, sd{0.0f, 1.0f};
     row_maxsum_pair(prow + v * A.S, true, prow + (N + v) * A.S, first >= 0, A.S, mt, md);
