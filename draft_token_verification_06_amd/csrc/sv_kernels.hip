@@ -23,6 +23,27 @@
 
 namespace sv {
 
+// Sum of v over the wave, valid in every lane, in a fixed order: within each
+// row of 16 lanes by DPP moves (swap neighbours, swap pairs, rotate by 4, by
+// 8), then the four row sums read from lanes 0, 16, 32 and 48 and added in
+// that order.  Every lane must be active.  The DPP moves and lane reads cost a
+// few cycles each, where a butterfly of lane shuffles goes through LDS six
+// times; that latency sits on the critical path of the latency-bound draws.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+__device__ __forceinline__ float wave_total(float v) {
+  v += dpp_move<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_move<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_move<0x124>(v);  // row_ror 4
+  v += dpp_move<0x128>(v);  // row_ror 8
+  return ((lane_value(v, 0) + lane_value(v, 16)) + lane_value(v, 32)) + lane_value(v, 48);
+}
+
 // Residual mass max(0, p - cq q) below which a draw counts it as none and
 // draws from p.  Weights are formed as 2^(x log2e - c) with offsets c of
 // magnitude ~10-60 rounded to float32, so two rows holding the same logits
@@ -589,7 +610,7 @@ __device__ __forceinline__ void chunk_sum_guarded(const SampleJob &job, int V, i
   float t = 0.0f;
 #pragma unroll
   for (int e = 0; e < G::E; ++e) t += w[e];
-  t = wave_sum(t);
+  t = wave_total(t);
   if ((tid & (kWave - 1)) == 0) wp[c * kFinWaves + tid / kWave] = t;
 }
 
@@ -616,7 +637,7 @@ __device__ __forceinline__ void batch_sums(const SampleJob &job, const uint4 *rt
 #pragma unroll
       for (int e = 0; e < EPV; ++e) t += bonus_weight(job, xt[e]);
     }
-    t = wave_sum(t);
+    t = wave_total(t);
     if ((tid & (kWave - 1)) == 0) wp[(c0 + u) * kFinWaves + tid / kWave] = t;
   }
 }
