@@ -44,6 +44,42 @@ __device__ __forceinline__ float wave_total(float v) {
   return ((lane_value(v, 0) + lane_value(v, 16)) + lane_value(v, 32)) + lane_value(v, 48);
 }
 
+// Inclusive prefix sum over the wave in lane order, every lane active: within
+// rows of 16 lanes by DPP row shifts by 1, 2, 4 and 8 (a lane shifted in from
+// outside its row reads 0), then the rows after the first add the running
+// total of the rows before them: lane 15 of rows 0 and 2 into rows 1 and 3,
+// then lane 31 into rows 2 and 3.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_rows(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, kRowMask, 0xF, false));
+}
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+  x += dpp_move<0x111>(x);    // row_shr 1
+  x += dpp_move<0x112>(x);    // row_shr 2
+  x += dpp_move<0x114>(x);    // row_shr 4
+  x += dpp_move<0x118>(x);    // row_shr 8
+  x += dpp_rows<0x142, 0xA>(x);  // row_bcast 15, into rows 1 and 3
+  x += dpp_rows<0x143, 0xC>(x);  // row_bcast 31, into rows 2 and 3
+  return x;
+}
+// The value of lane l - 1 in lane l, 0 in lane 0 (DPP wave_shr 1).
+__device__ __forceinline__ float wave_shift_up1(float x) { return dpp_move<0x138>(x); }
+
+// Largest int over the wave, read from lane 0 (every lane active): DPP within
+// rows of 16 lanes, then the four row maxima.
+template <int kCtrl>
+__device__ __forceinline__ int dpp_move_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, kCtrl, 0xF, 0xF, true);
+}
+__device__ __forceinline__ int wave_max_int(int v) {
+  v = max(v, dpp_move_i<0xB1>(v));
+  v = max(v, dpp_move_i<0x4E>(v));
+  v = max(v, dpp_move_i<0x124>(v));
+  v = max(v, dpp_move_i<0x128>(v));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
 // Residual mass max(0, p - cq q) below which a draw counts it as none and
 // draws from p.  Weights are formed as 2^(x log2e - c) with offsets c of
 // magnitude ~10-60 rounded to float32, so two rows holding the same logits
@@ -449,8 +485,7 @@ __device__ void tree_decide(const TreeArgs &A, int b, int v, bool write, SampleJ
       for (int u = s_parent[v]; ok && u > 0; u = s_parent[u]) ok = s_acc[u];
       if (ok) key = (static_cast<int>(A.meta.depth[v]) << 16) | (0xFFFF - v);
     }
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) key = max(key, __shfl_xor(key, off));
+    key = wave_max_int(key);
     if ((v & (kWave - 1)) == 0 && key >= 0) atomicMax(&s_key, key);  // one LDS atomic per wave
   }
   __syncthreads();
@@ -721,17 +756,12 @@ __device__ int draw_from_sums(const SampleJob &job, int V, int C, int h, const f
     for (int c0 = 0; c0 < C; c0 += kWave) {
       const int c = c0 + lane;
       const float x = c < C ? cs[c] : 0.0f;
-      float incl = x;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const float o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
+      float incl = wave_inclusive_scan(x);
       incl += carry;
       if (c < C) s_pref[c] = incl;
       const uint64_t mass = __ballot(c < C && x > 0.0f);
       if (mass) last_mass = c0 + 63 - __builtin_clzll(mass);
-      carry = __shfl(incl, kWave - 1);
+      carry = lane_value(incl, kWave - 1);
     }
     const float Z = carry;
     const float tau = job.v * Z;
@@ -760,14 +790,8 @@ __device__ int draw_from_sums(const SampleJob &job, int V, int C, int h, const f
 #pragma unroll
   for (int e = 0; e < G::E; ++e) ts += w[e];
   const int wave = tid / kWave, lane = tid & (kWave - 1);
-  float incl = ts;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const float o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
-  float excl = __shfl_up(incl, 1);
-  if (lane == 0) excl = 0.0f;
+  const float incl = wave_inclusive_scan(ts);
+  const float excl = wave_shift_up1(incl);  // 0 in lane 0
   if (lane == kWave - 1) s_wave_tot[wave] = incl;
   __syncthreads();
   float wave_off = 0.0f;
