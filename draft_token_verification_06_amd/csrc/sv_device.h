@@ -109,8 +109,9 @@ __device__ __forceinline__ float exp_shift(float x, float m_log2e) {
 }
 
 // ---------------------------------------------------------------------------
-// Combines.  Both are commutative and exact in their comparisons, so a fixed
-// butterfly gives every lane the same bits.
+// Combines of per-lane results (row maximum with the sum of exponentials, or
+// maximum with its first index).  The comparisons are exact; the wave
+// reductions below apply them in a fixed order.
 // ---------------------------------------------------------------------------
 struct MaxSum {
   float m, s;
@@ -136,22 +137,53 @@ __device__ __forceinline__ MaxIdx combine(MaxIdx a, MaxIdx b) {
   return (b.m > a.m || (b.m == a.m && b.i < a.i)) ? b : a;
 }
 
-__device__ __forceinline__ MaxSum wave_reduce(MaxSum v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    MaxSum o{__shfl_xor(v.m, off), __shfl_xor(v.s, off)};
-    v = combine(v, o);
-  }
-  return v;
+// Wave reductions: within each row of 16 lanes by DPP moves (swap neighbours,
+// swap pairs, rotate by 4, by 8), then the four row results, read from lanes
+// 0, 16, 32 and 48, combined in that order; every lane gets the result.  Every
+// lane must be active.  DPP moves and lane reads take a few cycles where a
+// butterfly of lane shuffles goes through LDS once per step.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, true));
+}
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, kCtrl, 0xF, 0xF, true);
+}
+__device__ __forceinline__ float read_lane_f32(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
+template <int kCtrl>
+__device__ __forceinline__ MaxSum dpp_step(MaxSum v) {
+  return combine(v, MaxSum{dpp_f32<kCtrl>(v.m), dpp_f32<kCtrl>(v.s)});
+}
+__device__ __forceinline__ MaxSum wave_reduce(MaxSum v) {
+  v = dpp_step<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v = dpp_step<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v = dpp_step<0x124>(v);  // row_ror 4
+  v = dpp_step<0x128>(v);  // row_ror 8
+  const MaxSum r0{read_lane_f32(v.m, 0), read_lane_f32(v.s, 0)};
+  const MaxSum r1{read_lane_f32(v.m, 16), read_lane_f32(v.s, 16)};
+  const MaxSum r2{read_lane_f32(v.m, 32), read_lane_f32(v.s, 32)};
+  const MaxSum r3{read_lane_f32(v.m, 48), read_lane_f32(v.s, 48)};
+  return combine(combine(r0, r1), combine(r2, r3));
+}
+
+template <int kCtrl>
+__device__ __forceinline__ MaxIdx dpp_step(MaxIdx v) {
+  return combine(v, MaxIdx{dpp_f32<kCtrl>(v.m), dpp_i32<kCtrl>(v.i)});
+}
 __device__ __forceinline__ MaxIdx wave_reduce(MaxIdx v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    MaxIdx o{__shfl_xor(v.m, off), __shfl_xor(v.i, off)};
-    v = combine(v, o);
-  }
-  return v;
+  v = dpp_step<0xB1>(v);
+  v = dpp_step<0x4E>(v);
+  v = dpp_step<0x124>(v);
+  v = dpp_step<0x128>(v);
+  const MaxIdx r0{read_lane_f32(v.m, 0), __builtin_amdgcn_readlane(v.i, 0)};
+  const MaxIdx r1{read_lane_f32(v.m, 16), __builtin_amdgcn_readlane(v.i, 16)};
+  const MaxIdx r2{read_lane_f32(v.m, 32), __builtin_amdgcn_readlane(v.i, 32)};
+  const MaxIdx r3{read_lane_f32(v.m, 48), __builtin_amdgcn_readlane(v.i, 48)};
+  return combine(combine(r0, r1), combine(r2, r3));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
