@@ -223,9 +223,11 @@ __device__ void window_decide(const WindowArgs &A, int b, int i, bool write, Sam
       if (k != n) out[k] = k < n ? x : -1;
   }
   // statistics and sampling uniform of row n, from lane n
-  MaxSum tn{__shfl(st.m, n & (kWave - 1)), __shfl(st.s, n & (kWave - 1))};
-  const MaxSum dn{__shfl(sd.m, n & (kWave - 1)), __shfl(sd.s, n & (kWave - 1))};
-  float v = __shfl(vi, n & (kWave - 1));
+  // n is the same in every lane: lane reads, not shuffles through LDS
+  const int ln = n & (kWave - 1);
+  MaxSum tn{lane_value(st.m, ln), lane_value(st.s, ln)};
+  const MaxSum dn{lane_value(sd.m, ln), lane_value(sd.s, ln)};
+  float v = lane_value(vi, ln);
   if (i == 0) {
     if (n >= kWave) {  // gamma = 64 with every draft accepted: row 64 has no lane
       tn = row_maxsum(prow + n * A.S, A.S);
@@ -338,9 +340,9 @@ __device__ __forceinline__ void stage_decide(const WindowArgs &A, int b, int i, 
       if (q != n) out[q] = q < n ? A.tokens[static_cast<int64_t>(b) * A.gamma + q] : -1;
   }
   const int src = (n - lo) & (kWave - 1);
-  const MaxSum tn{__shfl(st.m, src), __shfl(st.s, src)};
-  const MaxSum dn{__shfl(sd.m, src), __shfl(sd.s, src)};
-  const float v = __shfl(vi, src);
+  const MaxSum tn{lane_value(st.m, src), lane_value(st.s, src)};  // src is wave-uniform
+  const MaxSum dn{lane_value(sd.m, src), lane_value(sd.s, src)};
+  const float v = lane_value(vi, src);
   if (i == 0) {
     SampleJob jb{};
     jb.t_row = trow0 + n * row_bytes;
@@ -394,7 +396,7 @@ __global__ void __launch_bounds__(kWave) k_greedy_decide(GreedyArgs A) {
   const int am = i <= len ? am_row : 0;
   const uint64_t mask = __ballot(i < len && x != am);
   const int n = mask ? __builtin_ctzll(mask) : len;
-  int y = __shfl(am, n & (kWave - 1));
+  int y = __builtin_amdgcn_readlane(am, n & (kWave - 1));  // n is wave-uniform
   for (int k = i; k <= A.gamma; k += kWave)
     if (k != n) out[k] = k < n ? x : -1;
   if (i == 0) {

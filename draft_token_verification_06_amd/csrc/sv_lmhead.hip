@@ -391,7 +391,7 @@ __global__ void __launch_bounds__(kWave) k_lm_decide(LmDecideArgs A) {
   }
   for (int k = i; k <= g; k += kWave)
     if (k != n) out[k] = k < n ? A.tokens[rd + k] : -1;
-  float v = __shfl(uniform24(w.c1), n & (kWave - 1));
+  float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(uniform24(w.c1)), n & (kWave - 1)));
   if (i == 0) {
     if (n >= kWave) {  // gamma = 64 with every draft accepted: position 64 has no lane
       const U64x4 w2 = philox4x64_10({seq, static_cast<uint64_t>(base + 1 + n), 0, 0}, A.seed, A.tag);
