@@ -107,28 +107,40 @@ __device__ __forceinline__ MaxSum row_maxsum(const float2 *p, int S) {
   return r;
 }
 
-// The results of two rows (a target row and its draft row) at once, each
-// combined in segment order as row_maxsum does: both rows' loads go out
-// before either is combined, so the pair costs one row's round trips.  pa and
-// pb must point at S readable results whatever the flags: the loads are not
-// predicated per lane (a lane-predicated load waits for its data on its own),
-// and a row whose flag is false keeps the value it came with.
-__device__ __forceinline__ void row_maxsum_pair(const float2 *pa, bool la, const float2 *pb, bool lb, int S,
-                                                MaxSum &ra, MaxSum &rb) {
+// The results of several rows (a target row and its draft row, or two such
+// pairs) at once, each combined in segment order as row_maxsum does: every
+// row's loads go out before any is combined, so the set costs one row's round
+// trips.  Each pointer must address S readable results whatever its flag: the
+// loads are not predicated per lane (a lane-predicated load waits for its
+// data on its own), and a row whose flag is false keeps the value it came
+// with.
+template <int kRows>
+__device__ __forceinline__ void row_maxsum_rows(const float2 *const (&p)[kRows], const bool (&use)[kRows], int S,
+                                                MaxSum (&r)[kRows]) {
   for (int k0 = 0; k0 < S; k0 += kSegBatch) {
-    float2 qa[kSegBatch], qb[kSegBatch];
+    float2 q[kRows][kSegBatch];
 #pragma unroll
     for (int j = 0; j < kSegBatch; ++j)
       if (k0 + j < S) {
-        qa[j] = pa[k0 + j];
-        qb[j] = pb[k0 + j];
+#pragma unroll
+        for (int t = 0; t < kRows; ++t) q[t][j] = p[t][k0 + j];
       }
 #pragma unroll
-    for (int j = 0; j < kSegBatch; ++j) {
-      if (la && k0 + j < S) ra = k0 + j == 0 ? MaxSum{qa[j].x, qa[j].y} : combine(ra, MaxSum{qa[j].x, qa[j].y});
-      if (lb && k0 + j < S) rb = k0 + j == 0 ? MaxSum{qb[j].x, qb[j].y} : combine(rb, MaxSum{qb[j].x, qb[j].y});
-    }
+    for (int j = 0; j < kSegBatch; ++j)
+#pragma unroll
+      for (int t = 0; t < kRows; ++t)
+        if (use[t] && k0 + j < S)
+          r[t] = k0 + j == 0 ? MaxSum{q[t][j].x, q[t][j].y} : combine(r[t], MaxSum{q[t][j].x, q[t][j].y});
   }
+}
+__device__ __forceinline__ void row_maxsum_pair(const float2 *pa, bool la, const float2 *pb, bool lb, int S,
+                                                MaxSum &ra, MaxSum &rb) {
+  const float2 *const p[2] = {pa, pb};
+  const bool use[2] = {la, lb};
+  MaxSum r[2] = {ra, rb};
+  row_maxsum_rows<2>(p, use, S, r);
+  ra = r[0];
+  rb = r[1];
 }
 
 __device__ __forceinline__ MaxIdx row_argmax(const float2 *p, int S) {
@@ -1039,13 +1051,15 @@ __global__ void __launch_bounds__(kFinThreads) k_tree_walk(TreeArgs A) {
     const int first = A.meta.first_child[v];
     const int depth = A.meta.depth[v];
     const int rank = A.meta.rank[v];
-    // results of rows v and of the parent's rows w, each pair as one batch
+    // results of rows v and of the parent's rows w, all four as one batch
     const int w = v >= 1 ? A.meta.parent[v] : 0;
-    MaxSum mt{0.0f, 1.0f}, md{0.0f, 1.0f}, st{0.0f, 1.0f}, sd{0.0f, 1.0f};
-    row_maxsum_pair(prow + v * A.S, true, prow + (N + v) * A.S, first >= 0, A.S, mt, md);
-    row_maxsum_pair(prow + w * A.S, v >= 1, prow + (N + w) * A.S, v >= 1, A.S, st, sd);
-    s_ct[v] = norm_offset(mt);
-    s_cd[v] = first >= 0 ? norm_offset(md) : 0.0f;
+    const float2 *const rows4[4] = {prow + v * A.S, prow + (N + v) * A.S, prow + w * A.S, prow + (N + w) * A.S};
+    const bool use4[4] = {true, first >= 0, v >= 1, v >= 1};
+    MaxSum r4[4] = {{0.0f, 1.0f}, {0.0f, 1.0f}, {0.0f, 1.0f}, {0.0f, 1.0f}};
+    row_maxsum_rows<4>(rows4, use4, A.S, r4);
+    const MaxSum st = r4[2], sd = r4[3];
+    s_ct[v] = norm_offset(r4[0]);
+    s_cd[v] = first >= 0 ? norm_offset(r4[1]) : 0.0f;
     s_v[v] = uniform24(
         philox4x64_10({seq, static_cast<uint64_t>(base + depth + 1), static_cast<uint64_t>(rank), 0}, A.seed, A.tag)
             .c1);
