@@ -312,7 +312,7 @@ k_lm_gemm(LmGemmArgs P0, LmGemmArgs P1) {
 }
 
 // Per row, the column-tile partials in a fixed order: lane-strided, then the
-// wave butterfly.  One wave per row.
+// wave reduction.  One wave per row.
 __global__ void __launch_bounds__(256) k_lm_combine(const float2 *__restrict__ part, int NT, int M,
                                                     float2 *__restrict__ stats) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);

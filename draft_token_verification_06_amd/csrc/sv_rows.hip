@@ -5,8 +5,8 @@
 //   HBM with 16-byte loads and reduces it to (max, sum 2^((x-max) log2e)) or
 //   to (max, first index of the max).  Per-thread batches of kUnroll vectors
 //   are kept in registers: the batch maximum is taken first so that every
-//   element costs exactly one exponential, then wave butterflies and one LDS
-//   step finish the workgroup in a fixed order.
+//   element costs exactly one exponential, then DPP moves within each wave
+//   and one LDS step finish the workgroup in a fixed order.
 // k_probe_read: the same nontemporal loads over one contiguous buffer.
 #include "sv_device.h"
 #include "sv_rowset.h"
