@@ -10,7 +10,9 @@ the replacement drawn at a rejection of draft 0 follows the renormalised
 residual max(0, p_0 - q_0).  The expected laws come from scipy's softmax of the
 float32 rows the library reads; bins and threshold (10^-3) as in the oracle's
 pin at this size (test_oracle_chi2_large_vocab.py).  Power: the first tokens
-reject q_0 and the replacements reject p_0."""
+reject q_0 and the replacements reject p_0.  The second test draws the same
+10^5 windows as 2000 calls of 50 sequences, through the split draw (several
+workgroups per sequence's sampling pass, the last to finish searching)."""
 import numpy as np
 import pytest
 import torch
@@ -32,8 +34,8 @@ def _rows():
     return T, D
 
 
-def test_gpu_sampling_law_at_v32000():
-    print("GPU chi-square: 100 calls x 1000 windows, V=32000", flush=True)
+def _sampling_law(B, calls, draw_seed, philox_seed):
+    """10^5 windows as `calls` calls of B sequences; every law asserted."""
     T, D = _rows()
     Tf, Df = T.astype(np.float64), D.astype(np.float64)
     p = [sp_softmax(Tf[i]) for i in range(GAMMA + 1)]
@@ -42,14 +44,15 @@ def test_gpu_sampling_law_at_v32000():
     target = torch.from_numpy(T).to(DEV)[None].expand(B, GAMMA + 1, V).contiguous()
     draft = torch.from_numpy(D).to(DEV)[None].expand(B, GAMMA, V).contiguous()
     ws = sv.workspace(sv.SV_OP_WINDOW, B, GAMMA, V, torch.float32, DEV)
-    rng = np.random.default_rng(77)
+    rng = np.random.default_rng(draw_seed)
     n_all, out_all = [], []
-    for c in range(CALLS):
+    for c in range(calls):
         u = rng.random((B, GAMMA))
         toks = np.stack([np.minimum(V - 1, np.searchsorted(cq[i], u[:, i] * cq[i][-1], side="right"))
                          for i in range(GAMMA)], axis=1).astype(np.int32)
         sid = torch.arange(c * B, (c + 1) * B, dtype=torch.int64, device=DEV)
-        res = sv.verify_window(target, draft, torch.from_numpy(toks).to(DEV), seed=5, seq_ids=sid, ws=ws)
+        res = sv.verify_window(target, draft, torch.from_numpy(toks).to(DEV), seed=philox_seed, seq_ids=sid,
+                               ws=ws)
         n_all.append(res.n_accepted.cpu().numpy())
         out_all.append(res.out_tokens.cpu().numpy())
     n = np.concatenate(n_all)
@@ -71,3 +74,16 @@ def test_gpu_sampling_law_at_v32000():
         assert v > THRESHOLD, (k, v)
     for k, v in power.items():
         assert v < 1e-6, (k, v)
+
+
+def test_gpu_sampling_law_at_v32000():
+    print("GPU chi-square: 100 calls x 1000 windows, V=32000", flush=True)
+    _sampling_law(B, CALLS, 77, 5)
+
+
+def test_gpu_sampling_law_split_draw_at_v32000():
+    """The same laws through the split draw: at 50 sequences per call each
+    sequence's sampling pass is shared by 6 workgroups (float32 rows of
+    V = 32000 are 8 chunks) and the last to finish searches; 2000 calls."""
+    print("GPU chi-square, split draw: 2000 calls x 50 windows, V=32000", flush=True)
+    _sampling_law(50, 2000, 79, 7)
