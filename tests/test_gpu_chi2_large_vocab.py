@@ -12,7 +12,8 @@ float32 rows the library reads; bins and threshold (10^-3) as in the oracle's
 pin at this size (test_oracle_chi2_large_vocab.py).  Power: the first tokens
 reject q_0 and the replacements reject p_0.  The second test draws the same
 10^5 windows as 2000 calls of 50 sequences, through the split draw (several
-workgroups per sequence's sampling pass, the last to finish searching)."""
+workgroups per sequence's sampling pass, the last to finish searching); the
+third on bf16 logits."""
 import numpy as np
 import pytest
 import torch
@@ -34,16 +35,18 @@ def _rows():
     return T, D
 
 
-def _sampling_law(B, calls, draw_seed, philox_seed):
-    """10^5 windows as `calls` calls of B sequences; every law asserted."""
+def _sampling_law(B, calls, draw_seed, philox_seed, dtype=torch.float32):
+    """10^5 windows as `calls` calls of B sequences, logits stored as `dtype`;
+    the expected laws come from the stored values; every law asserted."""
     T, D = _rows()
-    Tf, Df = T.astype(np.float64), D.astype(np.float64)
+    Tt, Dt = torch.from_numpy(T).to(dtype), torch.from_numpy(D).to(dtype)
+    Tf, Df = Tt.double().numpy(), Dt.double().numpy()
     p = [sp_softmax(Tf[i]) for i in range(GAMMA + 1)]
     q = [sp_softmax(Df[i]) for i in range(GAMMA)]
     cq = [np.cumsum(x) for x in q]
-    target = torch.from_numpy(T).to(DEV)[None].expand(B, GAMMA + 1, V).contiguous()
-    draft = torch.from_numpy(D).to(DEV)[None].expand(B, GAMMA, V).contiguous()
-    ws = sv.workspace(sv.SV_OP_WINDOW, B, GAMMA, V, torch.float32, DEV)
+    target = Tt.to(DEV)[None].expand(B, GAMMA + 1, V).contiguous()
+    draft = Dt.to(DEV)[None].expand(B, GAMMA, V).contiguous()
+    ws = sv.workspace(sv.SV_OP_WINDOW, B, GAMMA, V, dtype, DEV)
     rng = np.random.default_rng(draw_seed)
     n_all, out_all = [], []
     for c in range(calls):
@@ -87,3 +90,10 @@ def test_gpu_sampling_law_split_draw_at_v32000():
     V = 32000 are 8 chunks) and the last to finish searches; 2000 calls."""
     print("GPU chi-square, split draw: 2000 calls x 50 windows, V=32000", flush=True)
     _sampling_law(50, 2000, 79, 7)
+
+
+def test_gpu_sampling_law_bf16_rows_at_v32000():
+    """The same laws on bf16 logits (the benchmark's storage type: its decode
+    and 8-element vectors in the sampling pass), 100 calls of 1000 sequences."""
+    print("GPU chi-square, bf16 rows: 100 calls x 1000 windows, V=32000", flush=True)
+    _sampling_law(B, CALLS, 81, 9, dtype=torch.bfloat16)
