@@ -13,7 +13,7 @@ pin at this size (test_oracle_chi2_large_vocab.py).  Power: the first tokens
 reject q_0 and the replacements reject p_0.  The second test draws the same
 10^5 windows as 2000 calls of 50 sequences, through the split draw (several
 workgroups per sequence's sampling pass, the last to finish searching); the
-third on bf16 logits."""
+third draws 10^6 windows on bf16 logits."""
 import numpy as np
 import pytest
 import torch
@@ -94,6 +94,8 @@ def test_gpu_sampling_law_split_draw_at_v32000():
 
 def test_gpu_sampling_law_bf16_rows_at_v32000():
     """The same laws on bf16 logits (the benchmark's storage type: its decode
-    and 8-element vectors in the sampling pass), 100 calls of 1000 sequences."""
-    print("GPU chi-square, bf16 rows: 100 calls x 1000 windows, V=32000", flush=True)
-    _sampling_law(B, CALLS, 81, 9, dtype=torch.bfloat16)
+    and 8-element vectors in the sampling pass) over 10^6 windows, 1000 calls of
+    1000 sequences: at this count a bin's probability is checked to about 1%
+    of itself."""
+    print("GPU chi-square, bf16 rows: 1000 calls x 1000 windows, V=32000", flush=True)
+    _sampling_law(B, 10 * CALLS, 81, 9, dtype=torch.bfloat16)
