@@ -76,15 +76,19 @@ def test_gpu_walk_first_token_follows_p_root():
     assert power < 1e-6
 
 
-def test_gpu_per_node_tree_first_token_law():
+@pytest.mark.parametrize("b,calls", [(B, CALLS), (50, 2000)])
+def test_gpu_per_node_tree_first_token_law(b, calls):
     """The per-node stochastic tree (SV_TREE_STOCHASTIC; "Accelerating LLM
     Inference with Staged Speculative Decoding", abstract) at V = 32000 with
     two children drawn i.i.d. from q_root: each child is tested against the
     root's rows on its own, so the first token's law is (1 - alpha) p + min(p, q)
     (alpha = sum min(p, q)), the closed form the oracle is pinned to by brute
-    force at V = 6.  10^5 trees; the same bins and threshold; power against
-    p_root itself."""
-    print("GPU per-node tree chi-square: 100 calls x 1000 trees, V=32000", flush=True)
+    force at V = 6.  10^5 trees as `calls` calls of b sequences: at b = 1000
+    one workgroup draws for each tree, at b = 50 six share each tree's sampling
+    pass and the last to finish searches; the same bins and threshold; power
+    against p_root itself."""
+    print(f"GPU per-node tree chi-square: {calls} calls x {b} trees, V=32000", flush=True)
+    B = b
     T, D = _rows()
     T, D = T[:3], D[:3]
     p0 = sp_softmax(T[0].astype(np.float64))
@@ -96,9 +100,9 @@ def test_gpu_per_node_tree_first_token_law():
     target = torch.from_numpy(np.ascontiguousarray(T)).to(DEV)[None].expand(B, N, V).contiguous()
     draft = torch.from_numpy(np.ascontiguousarray(D)).to(DEV)[None].expand(B, N, V).contiguous()
     ws = sv.workspace(sv.SV_OP_TREE, B, N, V, torch.float32, DEV)
-    rng = np.random.default_rng(66)
+    rng = np.random.default_rng(66 + b)
     first = []
-    for c in range(CALLS):
+    for c in range(calls):
         u = rng.random((B, 2))
         kids = np.minimum(V - 1, np.searchsorted(cq, u * cq[-1], side="right")).astype(np.int32)
         toks = np.concatenate([np.zeros((B, 1), np.int32), kids], axis=1)
