@@ -351,11 +351,18 @@ def rollback(buf_tokens, buf_len, stage, verified, verified_len, *, len_offset=0
 
 
 def probe_read(buf, sink=None):
-    """Streams buf through the library's read-bandwidth probe kernel."""
+    """Streams buf through the library's read-bandwidth probe kernel.  buf is
+    read as one contiguous byte range; sink takes one 32-bit word per
+    workgroup (sv_probe_blocks of the byte count)."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf: expected a contiguous device tensor")
     nbytes = buf.numel() * buf.element_size()
     nb = int(lib().sv_probe_blocks(nbytes))
     if sink is None:
         sink = torch.empty(nb, dtype=torch.int32, device=buf.device)
+    elif (sink.dtype not in (torch.int32, torch.uint32) or sink.device != buf.device
+          or not sink.is_contiguous() or sink.numel() < nb):
+        raise ValueError(f"sink: expected a contiguous 32-bit tensor of at least {nb} entries on {buf.device}")
     with torch.cuda.device(buf.device):
         _check(lib().sv_probe_read(_ptr(buf), nbytes, _ptr(sink), _stream(buf.device)))
     return sink

@@ -14,6 +14,7 @@ using namespace sv;
 namespace {
 
 constexpr int kVersion = 10100;  // 1.1.0
+constexpr int kWaveThreads = 64;  // threads of the one-wavefront launches (decisions, rollback)
 
 // The row list of a launch holds a full window's rows and a tree's target rows
 // plus its internal draft rows.
@@ -37,9 +38,10 @@ int check_workspace(void *ws, size_t bytes, size_t need) {
   return SV_OK;
 }
 
-// Row-statistics grids are one-dimensional with 32-bit block indices.
-bool grid_fits(int64_t B, const Layout &L) {
-  return B * L.rows_per_seq * L.plan.S < (int64_t(1) << 31);
+// The row-statistics grid (one workgroup per listed row and segment; a
+// layout's rows_per_seq bounds the rows a launch lists) fits a dispatch.
+bool rows_fit(int64_t B, const Layout &L) {
+  return grid_fits(B * L.rows_per_seq * L.plan.S, kRowThreads);
 }
 
 int launch_status() {
@@ -143,7 +145,7 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
   if (draft_seq_stride == 0) draft_seq_stride = d_rows;
   if (target_seq_stride < t_rows || draft_seq_stride < d_rows) return SV_EINVAL;
   const Layout L = make_layout(SV_OP_WINDOW, B, gamma, V);
-  if (!grid_fits(B, L)) return SV_EINVAL;
+  if (!rows_fit(B, L) || !grid_fits(B, kFinThreads)) return SV_EINVAL;
   const int ws = check_workspace(workspace, workspace_bytes, L.total);
   if (ws != SV_OK) return ws;
 
@@ -290,7 +292,7 @@ int sv_verify_greedy(const void *target_logits, int64_t target_seq_stride, int d
   if (target_seq_stride == 0) target_seq_stride = t_rows;
   if (target_seq_stride < t_rows) return SV_EINVAL;
   const Layout L = make_layout(SV_OP_GREEDY, B, gamma, V);
-  if (!grid_fits(B, L)) return SV_EINVAL;
+  if (!rows_fit(B, L) || !grid_fits(B, kWaveThreads)) return SV_EINVAL;
   const int ws = check_workspace(workspace, workspace_bytes, L.total);
   if (ws != SV_OK) return ws;
   float2 *part = reinterpret_cast<float2 *>(static_cast<char *>(workspace) + L.part_off);
@@ -351,7 +353,7 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
   if (sampled && !draft_logits) return SV_EINVAL;
   if (!aligned(target_logits, eb) || (draft_logits && !aligned(draft_logits, eb))) return SV_EINVAL;
   const Layout L = make_layout(SV_OP_TREE, B, N, V);
-  if (!grid_fits(B, L)) return SV_EINVAL;
+  if (!rows_fit(B, L) || !grid_fits(B, sampled ? kFinThreads : kTreeMaxNodes)) return SV_EINVAL;
   const int ws = check_workspace(workspace, workspace_bytes, L.total);
   if (ws != SV_OK) return ws;
   char *wsb = static_cast<char *>(workspace);
@@ -426,6 +428,7 @@ int sv_rollback(int32_t *buf_tokens, int32_t *buf_len, int32_t S, int32_t K,
   if (stage > 65535) return SV_EINVAL;
   if (!buf_tokens || !buf_len || !verified_tokens || !verified_len) return SV_EINVAL;
   if (verified_stride < 0) return SV_EINVAL;
+  if (!grid_fits(S, kWaveThreads)) return SV_EINVAL;
   RollbackArgs A{};
   A.buf_tokens = buf_tokens;
   A.buf_len = buf_len;
@@ -468,7 +471,11 @@ int sv_verify_window_lmhead(const void *hidden_target, const void *unembed_targe
       !aligned(unembed_draft, 16))
     return SV_EINVAL;
   const int64_t Mt = static_cast<int64_t>(B) * (gamma + 1), Md = static_cast<int64_t>(B) * gamma;
-  if (Mt + Md > (int64_t{1} << 30) || static_cast<int64_t>(lm_gemm_blocks(static_cast<int>(Mt), V)) > (1 << 30))
+  // grids: the GEMM (both problems), the combine (four rows per workgroup of
+  // 256), the decision (one wave per sequence) and the draw (1024 threads per
+  // sequence)
+  if (Mt + Md > (int64_t{1} << 30) || !grid_fits(lm_gemm_blocks(Mt, V) + lm_gemm_blocks(Md, V), kLmGemmThreads) ||
+      !grid_fits((Mt + Md + 3) / 4, 256) || !grid_fits(B, kFinThreads))
     return SV_EINVAL;
   const LmLayout L = make_lm_layout(B, gamma, V);
   const int ws = check_workspace(workspace, workspace_bytes, L.total);

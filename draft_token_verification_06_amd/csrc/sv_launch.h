@@ -96,7 +96,7 @@ struct LmDecideArgs {
 
 // Launches the GEMMs of two problems (target rows, draft rows) as one grid.
 void launch_lm_gemm(LmGemmArgs A0, LmGemmArgs A1, hipStream_t st);
-int lm_gemm_blocks(int M, int V);
+int64_t lm_gemm_blocks(int64_t M, int V);
 void launch_lm_combine(const float2 *part, int NT, int M, float2 *stats, hipStream_t st);
 void launch_lm_decide(const LmDecideArgs &A, int B, hipStream_t st);
 

@@ -38,6 +38,7 @@ constexpr int kWaveM = 64;                 // rows per wave: kBM / kWaveM waves 
 constexpr int kMT = kWaveM / 32;           // 32-row accumulator tiles per wave
 constexpr int kWavesM = kBM / kWaveM;
 constexpr int kGemmThreads = 64 * kWavesM * 2;
+static_assert(kGemmThreads == kLmGemmThreads, "the host checks grids against kLmGemmThreads");
 constexpr int kChunksK = kBK / 8;          // 16-byte chunks per row and K step
 constexpr int kLoadsA = kBM * kChunksK / kGemmThreads;
 constexpr int kLoadsW = kBN * kChunksK / kGemmThreads;
@@ -416,8 +417,8 @@ __global__ void __launch_bounds__(kWave) k_lm_decide(LmDecideArgs A) {
   }
 }
 
-int lm_gemm_blocks(int M, int V) {
-  const int RB = (M + kBM - 1) / kBM, NT = (V + kBN - 1) / kBN;
+int64_t lm_gemm_blocks(int64_t M, int V) {
+  const int64_t RB = (M + kBM - 1) / kBM, NT = (V + kBN - 1) / kBN;
   return 8 * ((NT + 7) / 8) * RB;
 }
 
@@ -426,8 +427,8 @@ void launch_lm_gemm(LmGemmArgs A0, LmGemmArgs A1, hipStream_t st) {
   A0.NT = (A0.V + kBN - 1) / kBN;
   A1.RB = (A1.M + kBM - 1) / kBM;
   A1.NT = (A1.V + kBN - 1) / kBN;
-  const int blocks = lm_gemm_blocks(A0.M, A0.V) + lm_gemm_blocks(A1.M, A1.V);
-  hipLaunchKernelGGL(k_lm_gemm, dim3(blocks), dim3(kGemmThreads), 0, st, A0, A1);
+  const int64_t blocks = lm_gemm_blocks(A0.M, A0.V) + lm_gemm_blocks(A1.M, A1.V);
+  hipLaunchKernelGGL(k_lm_gemm, dim3(static_cast<unsigned>(blocks)), dim3(kGemmThreads), 0, st, A0, A1);
 }
 
 void launch_lm_combine(const float2 *part, int NT, int M, float2 *stats, hipStream_t st) {

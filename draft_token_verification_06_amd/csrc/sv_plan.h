@@ -64,8 +64,16 @@ struct TreeMeta {
 };
 static_assert(sizeof(TreeMeta) <= 2560, "tree metadata travels in the kernel arguments");
 
-// LM-head fused path: vocabulary columns per GEMM block tile.
+// LM-head fused path: vocabulary columns per GEMM block tile, threads per
+// GEMM workgroup.
 constexpr int kLmBN = 256;
+constexpr int kLmGemmThreads = 512;
+
+// A dispatch packet gives each grid dimension's size in work-items as a 32-bit
+// count, so a launch of `blocks` workgroups of `threads` along one dimension
+// must stay within it; the entry points reject calls whose grids would not.
+constexpr int64_t kMaxGridItems = 0xFFFFFFFFll;
+inline bool grid_fits(int64_t blocks, int64_t threads) { return blocks >= 1 && blocks <= kMaxGridItems / threads; }
 
 struct RowPlan {
   int S;        // segments per row

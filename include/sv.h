@@ -37,6 +37,12 @@
  *     nodes of its depth (0 for windows).  `tag` separates the stages of a
  *     hierarchy.
  *   - Host-detectable errors return a negative sv_status and enqueue nothing.
+ *     Among them: sizes whose launches would not fit a dispatch, which counts
+ *     each grid dimension in 32-bit work-items (SV_EINVAL).  The row pass
+ *     takes 256 work-items per row segment, and rows are split into segments
+ *     only while a launch has fewer than 16,384 rows, so B times the rows per
+ *     sequence must stay below 2^24; calls that draw take 1024 work-items per
+ *     sequence, so B <= 4,194,303.
  *     Per-sequence data errors (a token outside [0, V), a window_len outside
  *     [0, gamma]) are found on the device and mark that sequence with
  *     n_accepted[b] = -1 and an all -1 row of out_tokens.  A launch failure

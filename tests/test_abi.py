@@ -131,6 +131,50 @@ def test_bad_host_arguments_return_status_without_device_work():
                                       fake, fake, None, None, None) == -6
 
 
+def test_grids_beyond_a_dispatch_are_rejected_on_the_host():
+    """A dispatch counts each grid dimension in 32-bit work-items.  Calls whose
+    row pass (256 work-items per row segment) or draw (1024 per sequence)
+    would not fit return SV_EINVAL before the workspace is examined; one
+    sequence fewer passes that check and meets the (deliberately too small)
+    workspace instead, SV_EWORKSPACE.  Nothing is launched either way."""
+    L = _lib.lib()
+    fake = ctypes.c_void_p(0x1000)
+
+    def window(B):
+        return L.sv_verify_window(fake, 0, fake, 0, 1, fake, None, B, 1, 8, 0, 0, None, None,
+                                  fake, fake, None, None, fake, 1 << 20, None)
+
+    # draw: 2^22 sequences x 1024 work-items = 2^32 (the row pass, 3 x 2^22 segments, fits)
+    assert window(1 << 22) == -1
+    assert window((1 << 22) - 1) == -3
+    assert L.sv_verify_window_early_exit(fake, 0, fake, 0, 1, fake, None, 1 << 22, 1, 8, 0, 0, None, None,
+                                         fake, fake, None, None, fake, 1 << 20, None) == -1
+
+    # row pass: B x 9 rows (gamma = 8, one segment at V = 8) x 256 work-items
+    def greedy(B):
+        return L.sv_verify_greedy(fake, 0, 1, fake, None, B, 8, 8, fake, fake, fake, 1 << 20, None)
+
+    limit = ((1 << 24) - 1) // 9
+    assert greedy(limit) == -3
+    assert greedy(limit + 1) == -1
+
+    # tree: 2N rows per sequence in the layout, 1024 work-items per sequence when sampling
+    par = (ctypes.c_int32 * 2)(-1, 0)
+    assert L.sv_verify_tree(fake, fake, 1, fake, par, 1 << 22, 2, 8, 1, 0, 0, None, None,
+                            fake, fake, fake, fake, fake, 1 << 20, None) == -1
+
+    # LM-head window: the draw's grid at 2^22 sequences
+    def lmhead(B):
+        return L.sv_verify_window_lmhead(fake, fake, 64, fake, fake, 64, fake, None, B, 1, 256,
+                                         0, 0, None, None, fake, fake, None, None, fake, 1 << 30, None)
+
+    assert lmhead(1 << 22) == -1
+    assert lmhead((1 << 22) - 1) == -3
+
+    # rollback: one wavefront per stream, 2^26 streams = 2^32 work-items
+    assert L.sv_rollback(fake, fake, 1 << 26, 3, 8, 1, fake, 8, fake, 0, None) == -1
+
+
 def test_binding_rejects_host_tensors_before_any_call():
     """The Python binding checks tensors on the host: logits, tokens and
     outputs in host memory are refused with ValueError, before the library is
@@ -153,3 +197,5 @@ def test_binding_rejects_host_tensors_before_any_call():
     with pytest.raises(ValueError):
         sv.rollback(torch.zeros(2, 3, 4, dtype=torch.int32), torch.zeros(2, 3, dtype=torch.int32), 1,
                     torch.zeros(2, 4, dtype=torch.int32), torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        sv.probe_read(torch.zeros(1024, dtype=torch.uint8))
