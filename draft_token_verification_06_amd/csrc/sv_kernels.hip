@@ -695,7 +695,10 @@ __device__ __forceinline__ void batch_sums(const SampleJob &job, const uint4 *rt
 // wp[c * kFinWaves + wave] = wave sum of chunk c.  Vector geometry: chunks
 // whose slots all lie in [0, V) go in batches of kFinBatch, the next batch's
 // loads in flight while the current one is reduced; the head chunk (h > 0)
-// and the row's end are masked per slot.
+// and the row's end are masked per slot.  The loads are ordinary cached
+// ones, not the row pass's nontemporal kind: the draw's in-chunk search reads
+// one chunk again, and the tree walk passes over the same row pair once per
+// rejected sibling, and those reads find the rows in L2.
 template <int DT, bool kVec>
 __device__ __forceinline__ void stream_chunk_sums(const SampleJob &job, int V, int c_begin, int c_end, int h,
                                                   float *wp, int tid) {
@@ -715,14 +718,14 @@ __device__ __forceinline__ void stream_chunk_sums(const SampleJob &job, int V, i
       uint4 at[kFinBatch], ad[kFinBatch], bt[kFinBatch], bd[kFinBatch];
 #pragma unroll
       for (int u = 0; u < kFinBatch; ++u) {
-        at[u] = load_stream(tv + (c + u) * kFinThreads);
-        ad[u] = resid ? load_stream(dv + (c + u) * kFinThreads) : zero;
+        at[u] = load_vec(tv + (c + u) * kFinThreads);
+        ad[u] = resid ? load_vec(dv + (c + u) * kFinThreads) : zero;
       }
       for (; c + 2 * kFinBatch <= full; c += kFinBatch) {
 #pragma unroll
         for (int u = 0; u < kFinBatch; ++u) {
-          bt[u] = load_stream(tv + (c + kFinBatch + u) * kFinThreads);
-          bd[u] = resid ? load_stream(dv + (c + kFinBatch + u) * kFinThreads) : zero;
+          bt[u] = load_vec(tv + (c + kFinBatch + u) * kFinThreads);
+          bd[u] = resid ? load_vec(dv + (c + kFinBatch + u) * kFinThreads) : zero;
         }
         batch_sums<DT>(job, at, ad, c, wp, tid);
 #pragma unroll
