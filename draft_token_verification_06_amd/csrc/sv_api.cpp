@@ -194,7 +194,7 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
     RowSet all = rs;
     all.add_target(0, gamma + 1);
     all.add_draft(0, gamma);
-    launch_row_stats(dtype, false, all, part, kRowCacheSmall, stream);
+    launch_row_stats(dtype, false, all, part, stream);
   }
   if (!(parts & (kPartFinish | kEarlyExit))) return launch_status();
   if (!(parts & kEarlyExit)) {
@@ -217,7 +217,7 @@ int window_impl(int parts, const void *target_logits, int64_t target_seq_stride,
     st.add_draft(lo, std::min(hi, static_cast<int>(gamma)));
     st.status = lo == 0 ? nullptr : status;
     st.arrive = lo == 0 ? ds.arrive : nullptr;  // every sequence has workgroups in the first block
-    launch_row_stats(dtype, false, st, part, kRowCacheBlock, stream);
+    launch_row_stats(dtype, false, st, part, stream);
     if (hi <= gamma) {
       launch_stage_decide(dtype, A, B, lo, hi, status, stream);
     } else {  // the last block is decided inside the draw
@@ -311,7 +311,7 @@ int sv_verify_greedy(const void *target_logits, int64_t target_seq_stride, int d
   rs.S = L.plan.S;
   rs.seg_len = L.plan.seg_len;
   rs.add_target(0, gamma + 1);
-  launch_row_stats(dtype, true, rs, part, kRowCacheSmall, stream);
+  launch_row_stats(dtype, true, rs, part, stream);
 
   GreedyArgs A{};
   A.tokens = draft_tokens;
@@ -385,7 +385,7 @@ int sv_verify_tree(const void *target_logits, const void *draft_logits, int dtyp
   if (sampled)
     for (int v = 0; v < N; ++v)
       if ((meta.internal[v >> 6] >> (v & 63)) & 1ull) rs.add_draft(v, v + 1);
-  launch_row_stats(dtype, !sampled, rs, part, kRowCacheSmall, stream);
+  launch_row_stats(dtype, !sampled, rs, part, stream);
   const int R = 2 * N;
 
   TreeArgs A{};

@@ -691,15 +691,21 @@ __device__ __forceinline__ void batch_sums(const SampleJob &job, const uint4 *rt
   }
 }
 
+template <bool kCached>
+__device__ __forceinline__ uint4 load_pass(const uint4 *p) {
+  if constexpr (kCached) return load_vec(p);
+  else return load_stream(p);
+}
+
 // Streams chunks [c_begin, c_end) of the job's row(s) once;
 // wp[c * kFinWaves + wave] = wave sum of chunk c.  Vector geometry: chunks
 // whose slots all lie in [0, V) go in batches of kFinBatch, the next batch's
 // loads in flight while the current one is reduced; the head chunk (h > 0)
-// and the row's end are masked per slot.  The loads are ordinary cached
-// ones, not the row pass's nontemporal kind: the draw's in-chunk search reads
-// one chunk again, and the tree walk passes over the same row pair once per
-// rejected sibling, and those reads find the rows in L2.
-template <int DT, bool kVec>
+// and the row's end are masked per slot.  The batches use nontemporal loads;
+// kCached selects ordinary cached ones instead, for the tree walk, whose
+// passes read the same row pair once per rejected sibling and find it in L2
+// from the second pass on.
+template <int DT, bool kVec, bool kCached = false>
 __device__ __forceinline__ void stream_chunk_sums(const SampleJob &job, int V, int c_begin, int c_end, int h,
                                                   float *wp, int tid) {
   int c = c_begin;
@@ -718,14 +724,14 @@ __device__ __forceinline__ void stream_chunk_sums(const SampleJob &job, int V, i
       uint4 at[kFinBatch], ad[kFinBatch], bt[kFinBatch], bd[kFinBatch];
 #pragma unroll
       for (int u = 0; u < kFinBatch; ++u) {
-        at[u] = load_vec(tv + (c + u) * kFinThreads);
-        ad[u] = resid ? load_vec(dv + (c + u) * kFinThreads) : zero;
+        at[u] = load_pass<kCached>(tv + (c + u) * kFinThreads);
+        ad[u] = resid ? load_pass<kCached>(dv + (c + u) * kFinThreads) : zero;
       }
       for (; c + 2 * kFinBatch <= full; c += kFinBatch) {
 #pragma unroll
         for (int u = 0; u < kFinBatch; ++u) {
-          bt[u] = load_vec(tv + (c + kFinBatch + u) * kFinThreads);
-          bd[u] = resid ? load_vec(dv + (c + kFinBatch + u) * kFinThreads) : zero;
+          bt[u] = load_pass<kCached>(tv + (c + kFinBatch + u) * kFinThreads);
+          bd[u] = resid ? load_pass<kCached>(dv + (c + kFinBatch + u) * kFinThreads) : zero;
         }
         batch_sums<DT>(job, at, ad, c, wp, tid);
 #pragma unroll
@@ -1150,8 +1156,8 @@ __global__ void __launch_bounds__(kFinThreads) k_tree_walk(TreeArgs A) {
     const bool vec = h >= 0;
     const int C = vec ? finish_chunks<DT, true>(V, h) : finish_chunks<DT, false>(V, 0);
     if (cmd != WALK_DRAW) {
-      if (vec) stream_chunk_sums<DT, true>(job, V, 0, C, h, s_wp, tid);
-      else stream_chunk_sums<DT, false>(job, V, 0, C, 0, s_wp, tid);
+      if (vec) stream_chunk_sums<DT, true, true>(job, V, 0, C, h, s_wp, tid);
+      else stream_chunk_sums<DT, false, true>(job, V, 0, C, 0, s_wp, tid);
       __syncthreads();
       chunk_totals(s_wp, 0, C, s_cs, tid);
       __syncthreads();

@@ -7,10 +7,6 @@
 //   are kept in registers: the batch maximum is taken first so that every
 //   element costs exactly one exponential, then DPP moves within each wave
 //   and one LDS step finish the workgroup in a fixed order.
-//   Launches that read at most the caller's cache limit of row bytes use
-//   ordinary cached loads: the draw (or the tree walk) reads some of those
-//   rows again right after and finds them in the caches; larger launches
-//   use nontemporal loads, which sustain more HBM read bandwidth.
 // k_probe_read: the same nontemporal loads over one contiguous buffer.
 #include "sv_device.h"
 #include "sv_rowset.h"
@@ -23,11 +19,6 @@ namespace sv {
 // 16-byte loads per thread per batch; the next batch is loaded while the
 // current one is reduced, so 2 * kUnroll loads are in flight per thread.
 constexpr int kUnroll = SV_ROW_UNROLL;
-template <bool kNT>
-__device__ __forceinline__ uint4 load_row(const uint4 *p) {
-  if constexpr (kNT) return load_stream(p);
-  else return load_vec(p);
-}
 
 // ---------------------------------------------------------------------------
 // Pass 1: row statistics
@@ -125,8 +116,8 @@ struct RowAcc<DT, true, U> {
 // a scalar tail.  Body vectors go in batches of U per thread (thread tid takes
 // vectors tid, tid + NT, ...); over full batches the next batch's loads are in
 // flight while the current batch is reduced, and a guarded remainder batch
-// fills its gaps with -inf.  kNT selects nontemporal loads.
-template <int DT, int NT, int U, bool kNT, typename Acc>
+// fills its gaps with -inf.
+template <int DT, int NT, int U, typename Acc>
 __device__ __forceinline__ void stream_segment(const char *row, int lo, int hi, int tid, Acc &acc) {
   using E = Elt<DT>;
   constexpr int EPV = E::kEPV;
@@ -142,11 +133,11 @@ __device__ __forceinline__ void stream_segment(const char *row, int lo, int hi, 
   if (nfull > 0) {
     uint4 cur[U], nxt[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) cur[u] = load_row<kNT>(vp + u * NT + tid);
+    for (int u = 0; u < U; ++u) cur[u] = load_stream(vp + u * NT + tid);
     for (int it = 0; it < nfull - 1; ++it) {
       const uint4 *q = vp + (it + 1) * kStep + tid;
 #pragma unroll
-      for (int u = 0; u < U; ++u) nxt[u] = load_row<kNT>(q + u * NT);
+      for (int u = 0; u < U; ++u) nxt[u] = load_stream(q + u * NT);
       float x[U * EPV];
 #pragma unroll
       for (int u = 0; u < U; ++u) E::vec(cur[u], x + u * EPV);
@@ -165,7 +156,7 @@ __device__ __forceinline__ void stream_segment(const char *row, int lo, int hi, 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int vi = nfull * kStep + u * NT + tid;
-      r[u] = vi < nvec ? load_row<kNT>(vp + vi) : neg;
+      r[u] = vi < nvec ? load_stream(vp + vi) : neg;
     }
     float x[U * EPV];
 #pragma unroll
@@ -176,7 +167,7 @@ __device__ __forceinline__ void stream_segment(const char *row, int lo, int hi, 
   for (int k = tail + tid; k < hi; k += NT) acc.one(E::one(row, k), k);
 }
 
-template <int DT, bool kArgmax, bool kNT>
+template <int DT, bool kArgmax>
 __global__ void __launch_bounds__(kRowThreads) k_row_stats(RowSet rs, float2 *__restrict__ part) {
   using E = Elt<DT>;
   const uint32_t blk = blockIdx.x;  // B * R * S < 2^31 (checked on the host)
@@ -211,7 +202,7 @@ __global__ void __launch_bounds__(kRowThreads) k_row_stats(RowSet rs, float2 *__
   const int hi = min(rs.V, lo + rs.seg_len);
   const int tid = threadIdx.x;
   RowAcc<DT, kArgmax> acc;
-  stream_segment<DT, kRowThreads, kUnroll, kNT>(row, lo, hi, tid, acc);
+  stream_segment<DT, kRowThreads, kUnroll>(row, lo, hi, tid, acc);
 
   __shared__ float lds_m[kRowThreads / kWave], lds_s[kRowThreads / kWave];
   float2 res = acc.result(lds_m, lds_s, tid);
@@ -262,29 +253,21 @@ __global__ void __launch_bounds__(kRowThreads) k_probe_read(const uint4 *__restr
 // ---------------------------------------------------------------------------
 // Launchers (host side)
 // ---------------------------------------------------------------------------
-template <bool kArgmax, bool kNT>
+template <bool kArgmax>
 static void launch_row_stats_t(int dtype, const RowSet &rs, float2 *part, hipStream_t st) {
   const int64_t blocks = static_cast<int64_t>(rs.B) * rs.R * rs.S;
   if (blocks < 1) return;
   const dim3 grid(static_cast<unsigned>(blocks)), block(kRowThreads);
   switch (dtype) {
-    case DT_BF16: hipLaunchKernelGGL((k_row_stats<DT_BF16, kArgmax, kNT>), grid, block, 0, st, rs, part); break;
-    case DT_F16: hipLaunchKernelGGL((k_row_stats<DT_F16, kArgmax, kNT>), grid, block, 0, st, rs, part); break;
-    default: hipLaunchKernelGGL((k_row_stats<DT_F32, kArgmax, kNT>), grid, block, 0, st, rs, part); break;
+    case DT_BF16: hipLaunchKernelGGL((k_row_stats<DT_BF16, kArgmax>), grid, block, 0, st, rs, part); break;
+    case DT_F16: hipLaunchKernelGGL((k_row_stats<DT_F16, kArgmax>), grid, block, 0, st, rs, part); break;
+    default: hipLaunchKernelGGL((k_row_stats<DT_F32, kArgmax>), grid, block, 0, st, rs, part); break;
   }
 }
 
-void launch_row_stats(int dtype, bool argmax, const RowSet &rs, float2 *part, int64_t cache_limit,
-                      hipStream_t st) {
-  const int64_t row_bytes = static_cast<int64_t>(rs.B) * rs.R * rs.V * (dtype == DT_F32 ? 4 : 2);
-  const bool nt = row_bytes > cache_limit;
-  if (argmax) {
-    if (nt) launch_row_stats_t<true, true>(dtype, rs, part, st);
-    else launch_row_stats_t<true, false>(dtype, rs, part, st);
-  } else {
-    if (nt) launch_row_stats_t<false, true>(dtype, rs, part, st);
-    else launch_row_stats_t<false, false>(dtype, rs, part, st);
-  }
+void launch_row_stats(int dtype, bool argmax, const RowSet &rs, float2 *part, hipStream_t st) {
+  if (argmax) launch_row_stats_t<true>(dtype, rs, part, st);
+  else launch_row_stats_t<false>(dtype, rs, part, st);
 }
 
 int probe_blocks(size_t bytes) {

@@ -51,19 +51,8 @@ struct RowSet {
 // Per-sequence state of the early-exit window (workspace): verifying, or done.
 constexpr int32_t kSeqVerifying = -2;
 
-// Row bytes of a launch up to which the row pass reads with ordinary cached
-// loads instead of nontemporal ones, so that the draw's second read of a
-// sequence's row pair finds it in the caches.  kRowCacheSmall for launches
-// that are latency bound anyway; kRowCacheBlock for an early-exit position
-// block, whose rows the draw reads again for every sequence that stops in
-// that block (half the 256 MiB Infinity Cache).
-constexpr int64_t kRowCacheSmall = int64_t{32} << 20;
-constexpr int64_t kRowCacheBlock = int64_t{128} << 20;
-
-// Grid: B * R * S workgroups, formed from rs; cached loads up to cache_limit
-// row bytes.
-void launch_row_stats(int dtype, bool argmax, const RowSet &rs, float2 *part, int64_t cache_limit,
-                      hipStream_t st);
+// Grid: B * R * S workgroups, formed from rs.
+void launch_row_stats(int dtype, bool argmax, const RowSet &rs, float2 *part, hipStream_t st);
 int probe_blocks(size_t bytes);
 void launch_probe_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t st);
 
