@@ -597,23 +597,37 @@ def side_workloads(torch, sv, synth, dev):
     out["window_B8_g8_V128256_bf16_graph_replay"] = {"us": event_time_ms(torch, graph.replay, reps) * 1e3}
     del graph, d, w, o
 
-    # tree (4, 3, 2), B=4, V=50257 fp16
+    # tree (4, 3, 2), B=4, V=50257 fp16.  The multi-candidate walk reads its
+    # rows with cached loads, so its inputs rotate over distinct copies: a
+    # call must not find the previous call's rows in the caches.
     d = synth.tree_config3(device=dev)
     w = sv.workspace(sv.SV_OP_TREE, 4, 41, 50257, torch.float16, dev)
-    for mode in ("greedy", "stochastic", "multi_candidate"):
+    for mode in ("greedy", "stochastic"):
         ms = event_time_ms(torch, lambda: sv.verify_tree(d["target"], d["draft"], d["tokens"], d["parent"],
                                                          mode=mode, ws=w), reps)
         out[f"tree_432_B4_V50257_f16_{mode}"] = {"us": ms * 1e3}
+    def rotating_walk(copies, ws):
+        it = iter(range(10 ** 9))
+
+        def call():
+            x = copies[next(it) % len(copies)]
+            sv.verify_tree(x["target"], x["draft"], x["tokens"], x["parent"], mode="multi_candidate", ws=ws)
+        return call
+
+    copies = [d] + [synth.tree_config3(seed=1003 + 7 * k, device=dev) for k in range(1, 32)]
+    ms = event_time_ms(torch, rotating_walk(copies, w), reps)
+    out["tree_432_B4_V50257_f16_multi_candidate"] = {"us": ms * 1e3, "input_copies": 32}
+    del copies
     # the multi-candidate walk with frequent sibling rejections (draft noise sd 2)
-    d = synth.tree_batch(32, synth.bfs_tree((4, 3, 2)), 50257, dtype="f16", sigma=2.0, seed=1013,
-                         device=dev)
+    copies = [synth.tree_batch(32, synth.bfs_tree((4, 3, 2)), 50257, dtype="f16", sigma=2.0, seed=1013 + k,
+                               device=dev) for k in range(4)]
+    d = copies[0]
     w = sv.workspace(sv.SV_OP_TREE, 32, 41, 50257, torch.float16, dev)
-    ms = event_time_ms(torch, lambda: sv.verify_tree(d["target"], d["draft"], d["tokens"], d["parent"],
-                                                     mode="multi_candidate", ws=w), reps)
+    ms = event_time_ms(torch, rotating_walk(copies, w), reps)
     r = sv.verify_tree(d["target"], d["draft"], d["tokens"], d["parent"], mode="multi_candidate", ws=w)
     out["tree_432_B32_V50257_f16_sigma2_multi_candidate"] = {
-        "us": ms * 1e3, "mean_depth": float(r.n_accepted.float().mean().item())}
-    del d, w
+        "us": ms * 1e3, "mean_depth": float(r.n_accepted.float().mean().item()), "input_copies": 4}
+    del d, w, copies
 
     # LM head fused with the window (8B-shaped target Ht=4096, 1B-shaped draft Hd=2048)
     Bl, Ht, Hd = 256, 4096, 2048
