@@ -49,10 +49,10 @@ template <> struct Elt<DT_BF16> {
   static constexpr int kBytes = 2;
   static constexpr int kEPV = 8;
   static constexpr uint32_t kNegInfPair = 0xFF80FF80u;  // two bf16 -inf
-  __device__ static __forceinline__ float one(const void *row, int64_t i) {
-    const uint32_t r = as_global<uint16_t>(row)[i];
-    return __uint_as_float(r << 16);
-  }
+  // raw(): the element's bits, dec(): their value; one() = dec(raw()).
+  __device__ static __forceinline__ uint32_t raw(const void *row, int64_t i) { return as_global<uint16_t>(row)[i]; }
+  __device__ static __forceinline__ float dec(uint32_t r) { return __uint_as_float(r << 16); }
+  __device__ static __forceinline__ float one(const void *row, int64_t i) { return dec(raw(row, i)); }
   __device__ static __forceinline__ void vec(const uint4 &r, float *x) {
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
@@ -70,9 +70,9 @@ template <> struct Elt<DT_F16> {
   __device__ static __forceinline__ float h2f(uint32_t bits) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
   }
-  __device__ static __forceinline__ float one(const void *row, int64_t i) {
-    return h2f(as_global<uint16_t>(row)[i]);
-  }
+  __device__ static __forceinline__ uint32_t raw(const void *row, int64_t i) { return as_global<uint16_t>(row)[i]; }
+  __device__ static __forceinline__ float dec(uint32_t r) { return h2f(r); }
+  __device__ static __forceinline__ float one(const void *row, int64_t i) { return dec(raw(row, i)); }
   __device__ static __forceinline__ void vec(const uint4 &r, float *x) {
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
@@ -87,9 +87,9 @@ template <> struct Elt<DT_F32> {
   static constexpr int kBytes = 4;
   static constexpr int kEPV = 4;
   static constexpr uint32_t kNegInfPair = 0xFF800000u;  // one f32 -inf
-  __device__ static __forceinline__ float one(const void *row, int64_t i) {
-    return as_global<float>(row)[i];
-  }
+  __device__ static __forceinline__ uint32_t raw(const void *row, int64_t i) { return as_global<uint32_t>(row)[i]; }
+  __device__ static __forceinline__ float dec(uint32_t r) { return __uint_as_float(r); }
+  __device__ static __forceinline__ float one(const void *row, int64_t i) { return dec(raw(row, i)); }
   __device__ static __forceinline__ void vec(const uint4 &r, float *x) {
     x[0] = __uint_as_float(r.x);
     x[1] = __uint_as_float(r.y);

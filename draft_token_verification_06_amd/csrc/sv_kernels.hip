@@ -212,13 +212,21 @@ __device__ void window_decide(const WindowArgs &A, int b, int i, bool write, Sam
   const char *trow0 = A.t + b * A.t_stride_bytes;
   const char *drow0 = A.d + b * A.d_stride_bytes;
   const int64_t row_bytes = static_cast<int64_t>(A.V) * E::kBytes;
+  // the two logits at the draft token go out before the uniforms are
+  // computed, from every lane (lanes past the window read token 0 of row
+  // min(i, gamma - 1) and do not use it), so the Philox rounds run while
+  // they are in flight
+  const int ig = min(i, A.gamma - 1);
+  const uint32_t traw = E::raw(trow0 + ig * row_bytes, x);
+  const uint32_t draw = E::raw(drow0 + ig * row_bytes, x);
+  __builtin_amdgcn_sched_barrier(0);  // keeps the two loads ahead of the rounds
   const U64x4 w = philox4x64_10({seq, static_cast<uint64_t>(base + 1 + i), 0, 0}, A.seed, A.tag);
   const float vi = uniform24(w.c1);
   float P = 0.0f, Q = 0.0f;
   bool acc = false;
   if (i < len) {
-    P = prob_at(E::one(trow0 + i * row_bytes, x), st);
-    Q = prob_at(E::one(drow0 + i * row_bytes, x), sd);
+    P = prob_at(E::dec(traw), st);
+    Q = prob_at(E::dec(draw), sd);
     acc = uniform24(w.c0) * Q < P;
   }
   const uint64_t inv = ~static_cast<uint64_t>(__ballot(acc));
@@ -319,13 +327,19 @@ __device__ __forceinline__ void stage_decide(const WindowArgs &A, int b, int i, 
   const char *drow0 = A.d + b * A.d_stride_bytes;
   const int64_t row_bytes = static_cast<int64_t>(A.V) * E::kBytes;
   const int cnt = min(hi, len) - lo;  // positions examined in this block
+  // token logits first, from every lane (see window_decide), then the uniforms
+  const int pg = min(p, A.gamma - 1);
+  const int xg = i < cnt ? xp : 0;
+  const uint32_t traw = E::raw(trow0 + pg * row_bytes, xg);
+  const uint32_t draw = E::raw(drow0 + pg * row_bytes, xg);
+  __builtin_amdgcn_sched_barrier(0);
   const U64x4 w = philox4x64_10({seq, static_cast<uint64_t>(base + 1 + p), 0, 0}, A.seed, A.tag);
   const float vi = uniform24(w.c1);
   float P = 0.0f, Q = 0.0f;
   bool acc = false;
   if (i < cnt) {
-    P = prob_at(E::one(trow0 + p * row_bytes, xp), st);
-    Q = prob_at(E::one(drow0 + p * row_bytes, xp), sd);
+    P = prob_at(E::dec(traw), st);
+    Q = prob_at(E::dec(draw), sd);
     acc = uniform24(w.c0) * Q < P;
   }
   const uint64_t inv = ~static_cast<uint64_t>(__ballot(acc));
@@ -1060,8 +1074,12 @@ __global__ void __launch_bounds__(kFinThreads) k_tree_walk(TreeArgs A) {
     const int first = A.meta.first_child[v];
     const int depth = A.meta.depth[v];
     const int rank = A.meta.rank[v];
-    // results of rows v and of the parent's rows w, all four as one batch
+    // the token's logits in the parent's rows (the root reads token 0 of row
+    // 0 and does not use it), then the results of rows v and of the parent's
+    // rows w, all four as one batch; the Philox rounds run while they land
     const int w = v >= 1 ? A.meta.parent[v] : 0;
+    const uint32_t traw = E::raw(t0 + w * row_bytes, tok);
+    const uint32_t draw = E::raw(d0 + w * row_bytes, tok);
     const float2 *const rows4[4] = {prow + v * A.S, prow + (N + v) * A.S, prow + w * A.S, prow + (N + w) * A.S};
     const bool use4[4] = {true, first >= 0, v >= 1, v >= 1};
     MaxSum r4[4] = {{0.0f, 1.0f}, {0.0f, 1.0f}, {0.0f, 1.0f}, {0.0f, 1.0f}};
@@ -1073,8 +1091,8 @@ __global__ void __launch_bounds__(kFinThreads) k_tree_walk(TreeArgs A) {
         philox4x64_10({seq, static_cast<uint64_t>(base + depth + 1), static_cast<uint64_t>(rank), 0}, A.seed, A.tag)
             .c1);
     if (v >= 1) {
-      s_P[v] = prob_at(E::one(t0 + w * row_bytes, tok), st);
-      s_Q[v] = prob_at(E::one(d0 + w * row_bytes, tok), sd);
+      s_P[v] = prob_at(E::dec(traw), st);
+      s_Q[v] = prob_at(E::dec(draw), sd);
       s_u[v] = uniform24(
           philox4x64_10({seq, static_cast<uint64_t>(base + depth), static_cast<uint64_t>(rank), 0}, A.seed, A.tag)
               .c0);
