@@ -64,7 +64,7 @@ CPU_SAMPLE_MAX_ROUNDS = 40
 # each scaled by the same counter on the 1 GiB copy this script performs
 # (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000).  Valid for the kernel sources whose
 # hash is recorded; reported as null for any other build.
-PMC_TRAFFIC = {"kernel_sha": "0f1c68980b5eb44d", "bytes": 1117005352}
+PMC_TRAFFIC = {"kernel_sha": "b2ec83fa76865b03", "bytes": 1117005352}
 
 
 def kernel_sha():
